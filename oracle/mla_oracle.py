@@ -1,0 +1,367 @@
+"""fp64 CPU oracle for weight-absorbed Multi-head Latent Attention.
+
+Test infrastructure: only tests/, the smoke check and the benchmark's
+CPU-baseline leg use this module. It is deliberately plain and slow.
+
+Sources (the pages are cited by title and part, never by line):
+  [ferrox]   docs.rs, ferrox-core 0.23.0, src/mla_absorbed.rs: module
+             documentation (score / out_lat / v formulas, kq_scale rule),
+             the function `causal_mla_absorbed_attention` (layouts, two-pass
+             softmax with an empty-sum guard) and its unit test
+             `absorbed_equals_naive_for_the_same_kv_b` (kv_b row layout,
+             per-head expansion, tolerances).
+  [notebook] Colab gist "MLA_RoPE-less.ipynb": head split, full matrix
+             absorption (W_aQK, W_aVO), cache append, printed shapes.
+  [lab]      lynx-cortex "Lab 01 - MLA math exercise", Bloque A (cache size
+             per token) and Bloque B (the identity q^T W_UK c = (W_UK^T q)^T c).
+  [gated]    tensortonic "Kimi K3 step 2: Gated MLA": problem statement,
+             worked example, causal-mask hint.
+  [tutorial] uithub preacher-1/MLA_tutorial, formula.md Part 3: training form
+             (per-head k, v from c) and inference form (absorbed q, shared
+             key [c, k_pe], value c, causal sum over i <= t).
+
+Readings adopted where the pages are silent (each listed in the design doc):
+  * logits are scaled by kq_scale = 1/sqrt(d_nope + d_r) ([ferrox] module
+    doc); the tutorial's formula omits the scale and the notebook has no
+    softmax at all;
+  * causal alignment is bottom-right: query i of S_q sees cache positions
+    t <= i + S_kv - S_q (the diagonal included, [gated] hint 2);
+  * lse is the natural log of the softmax denominator, max included; an
+    empty visible range gives a zero output and lse = -inf ([ferrox] guard).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "attend_one_head", "expand_per_head", "mla_unabsorbed", "latent_attention",
+    "latent_attention_expanded_v", "absorb_query", "up_project",
+    "causal_visible", "latent_prefill_causal", "lse_merge",
+    "mha_cache_values_per_token", "mla_cache_values_per_token", "cache_ratio",
+    "notebook_split_heads", "notebook_linear_absorbed", "notebook_linear_unabsorbed",
+    "notebook_softmax_unabsorbed", "gated_mla",
+]
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# the attention definition
+# --------------------------------------------------------------------------
+def attend_one_head(q, K, V, scale, n_visible):
+    """Scaled dot-product softmax attention of one query over one head's cache.
+
+    q [d_k], K [T, d_k], V [T, d_v]; only positions 0..n_visible-1 take part.
+    Logits s_t = (q . K_t) * scale; softmax by subtracting the max,
+    exponentiating and dividing by the sum, as `causal_mla_absorbed_attention`
+    does ([ferrox]); output = sum_t p_t V_t. Nothing visible => zeros, -inf.
+    Returns (out [d_v], lse) with lse = max + log(sum exp(s - max)).
+    Pinned by: brute-force scalar loops, the two-token closed form, the
+    single-position example of [gated], shift and permutation invariances.
+    """
+    q, K, V = _f64(q), _f64(K), _f64(V)
+    n = int(n_visible)
+    if n <= 0:
+        return np.zeros(V.shape[1]), -math.inf
+    s = (K[:n] @ q) * scale
+    m = s.max()
+    e = np.exp(s - m)
+    z = e.sum()
+    p = e / z
+    return p @ V[:n], float(m + math.log(z))
+
+
+def expand_per_head(latent, d_c, w_uk=None, w_uv=None, H=None):
+    """Per-head key and value caches from the latent rows (the "naive" form).
+
+    latent [T, d_c + d_r] rows [c_t | k_pe_t]. With weights (kv_b rows of
+    [ferrox]'s test: W_UK[h] [d_nope, d_c], W_UV[h] [d_v, d_c]):
+        k[t,h] = [W_UK[h] c_t , k_pe_t],   v[t,h] = W_UV[h] c_t
+    as the test expands every position through kv_b and the tutorial's
+    training form builds k, v per head from c. Without W_UK (the query is
+    already in latent coordinates) the key of every head is the shared row
+    [c_t | k_pe_t]; without W_UV the value of every head is c_t ([ferrox]
+    module doc: one shared key per position, value a prefix of it).
+    Returns K [T, H, d_k], V [T, H, d_v] in the [seq, n_heads, dim] layout.
+    """
+    latent = _f64(latent)
+    c, k_pe = latent[:, :d_c], latent[:, d_c:]
+    T = latent.shape[0]
+    if w_uk is not None:
+        w_uk = _f64(w_uk)
+        H = w_uk.shape[0]
+        k_nope = np.einsum("hij,tj->thi", w_uk, c)
+        K = np.concatenate([k_nope, np.broadcast_to(k_pe[:, None, :], (T, H, k_pe.shape[1]))], axis=2)
+    else:
+        K = np.repeat(latent[:, None, :], H, axis=1)
+    if w_uv is not None:
+        w_uv = _f64(w_uv)
+        V = np.einsum("hij,tj->thi", w_uv, c)
+    else:
+        V = np.repeat(c[:, None, :], H, axis=1)
+    return K, V
+
+
+def mla_unabsorbed(q_nope, q_pe, latent, d_c, w_uk, w_uv, scale, n_visible):
+    """Unabsorbed MLA for one query token: expand K, V per head, then attend.
+
+    q_nope [H, d_nope], q_pe [H, d_r]; per-head query [q_nope | q_pe] against
+    k[t,h] = [W_UK[h] c_t | k_pe_t] and values W_UV[h] c_t ([ferrox] test,
+    naive branch; [tutorial] training form). Returns (v [H, d_v], lse [H]).
+    Pinned by: equality with the absorbed chain on the [ferrox] test inputs
+    and on the notebook workload, and the wrong-scale check of that test.
+    """
+    q = np.concatenate([_f64(q_nope), _f64(q_pe)], axis=1)
+    K, V = expand_per_head(latent, d_c, w_uk, w_uv)
+    H = q.shape[0]
+    out = np.zeros((H, V.shape[2]))
+    lse = np.full(H, -math.inf)
+    for h in range(H):
+        out[h], lse[h] = attend_one_head(q[h], K[:, h, :], V[:, h, :], scale, n_visible)
+    return out, lse
+
+
+def latent_attention(q, latent, d_c, scale, n_visible, heads=None):
+    """Attention of absorbed queries over the latent cache (the definition).
+
+    q [H, d_c + d_r] rows [q_abs | q_pe]; latent [T, d_c + d_r]. Each head's
+    key is the shared row [c_t | k_pe_t] and its value is c_t, so
+        score[h,t] = (q_abs[h].c_t + q_pe[h].k_pe_t) * scale
+        out_lat[h] = sum_t softmax(score[h])_t c_t
+    ([ferrox] module doc; [tutorial] inference form). `heads` restricts the
+    computation to a subset of heads (sampled checks at large sizes).
+    Returns (out_lat [len(heads), d_c], lse [len(heads)]).
+    Pinned by: the absorbed == unabsorbed equality, one-position output = c_0,
+    q = 0 => mean of c, shift/permutation invariance, brute-force loops.
+    """
+    q, latent = _f64(q), _f64(latent)
+    heads = range(q.shape[0]) if heads is None else heads
+    heads = list(heads)
+    out = np.zeros((len(heads), d_c))
+    lse = np.full(len(heads), -math.inf)
+    K = latent               # the key row of every head
+    V = latent[:, :d_c]      # the value of every head
+    for i, h in enumerate(heads):
+        out[i], lse[i] = attend_one_head(q[h], K, V, scale, n_visible)
+    return out, lse
+
+
+def latent_attention_expanded_v(q, latent, d_c, w_uv, scale, n_visible, heads=None):
+    """As latent_attention, but with the value expanded per head: v_t = W_UV[h] c_t.
+
+    This is the output after the up-projection computed the unabsorbed way
+    (values expanded before the weighted sum; [ferrox] test, naive branch).
+    Returns (v [len(heads), d_v], lse).
+    """
+    q, latent, w_uv = _f64(q), _f64(latent), _f64(w_uv)
+    heads = list(range(q.shape[0]) if heads is None else heads)
+    out = np.zeros((len(heads), w_uv.shape[1]))
+    lse = np.full(len(heads), -math.inf)
+    c = latent[:, :d_c]
+    for i, h in enumerate(heads):
+        Vh = c @ w_uv[h].T
+        out[i], lse[i] = attend_one_head(q[h], latent, Vh, scale, n_visible)
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# the per-head products around the attention
+# --------------------------------------------------------------------------
+def absorb_query(q_nope, q_pe, w_uk):
+    """q_abs[..., h, j] = sum_i W_UK[h, i, j] q_nope[..., h, i]; then [q_abs | q_pe].
+
+    W_UK[h] is the k_b block of kv_b, [d_nope, d_c] ([ferrox] test, absorbed
+    branch: the query pushed through k_b); it is W_UK^T q of the [lab]
+    identity and q W_qc W_kc^T of the [tutorial] inference form.
+    Pinned by: the [lab] identity q^T W_UK c = (W_UK^T q)^T c on random
+    inputs and the absorbed == unabsorbed equality.
+    """
+    q_nope, w_uk = _f64(q_nope), _f64(w_uk)
+    q_abs = np.einsum("hij,...hi->...hj", w_uk, q_nope)
+    if q_pe is None:
+        return q_abs
+    return np.concatenate([q_abs, _f64(q_pe)], axis=-1)
+
+
+def up_project(out_lat, w_uv):
+    """v[..., h, i] = sum_j W_UV[h, i, j] out_lat[..., h, j] (W_UV[h] = v_b, [d_v, d_c]).
+
+    [ferrox] module doc: v[h] = wv_b[h] . out_lat[h]; [tutorial] inference
+    form: o_t^(s) W_v^(s). Pinned by: the absorbed == unabsorbed equality and
+    associativity with the per-head expanded values.
+    """
+    return np.einsum("hij,...hj->...hi", _f64(w_uv), _f64(out_lat))
+
+
+# --------------------------------------------------------------------------
+# causal prefill
+# --------------------------------------------------------------------------
+def causal_visible(i, S_q, S_kv):
+    """Number of cache positions query i may see: t <= i + S_kv - S_q, clamped to [0, S_kv]."""
+    return int(min(max(i + 1 + S_kv - S_q, 0), S_kv))
+
+
+def latent_prefill_causal(q, latent, d_c, scale, rows=None, heads=None):
+    """Causal latent attention for a chunk of S_q queries over S_kv cache rows.
+
+    q [S_q, H, W], latent [S_kv, W]. Query i attends to the cache positions
+    the causal mask leaves visible ([gated]: later positions are masked
+    before the softmax; [tutorial]: sums over i <= t). `rows` restricts the
+    queries computed. Returns (out_lat [len(rows), H', d_c], lse [len(rows), H']).
+    """
+    q = _f64(q)
+    S_q = q.shape[0]
+    S_kv = np.asarray(latent).shape[0]
+    rows = list(range(S_q) if rows is None else rows)
+    hs = list(range(q.shape[1]) if heads is None else heads)
+    out = np.zeros((len(rows), len(hs), d_c))
+    lse = np.full((len(rows), len(hs)), -math.inf)
+    for r, i in enumerate(rows):
+        out[r], lse[r] = latent_attention(q[i], latent, d_c, scale, causal_visible(i, S_q, S_kv), hs)
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# merging results over disjoint position ranges
+# --------------------------------------------------------------------------
+def lse_merge(outs, lses):
+    """Merge softmax results computed over disjoint position ranges.
+
+    outs [P, ..., d] (each normalised over its own range), lses [P, ...].
+    lse = log sum_s exp(lse_s); out = sum_s exp(lse_s - lse) out_s. Ranges
+    with lse_s = -inf contribute nothing; all empty => zeros and -inf.
+    This is the exact identity behind splitting the positions of one query
+    (no page states it; the split-sequence decode needs it). Pinned by:
+    merging the oracle's attention over sub-ranges equals the oracle's
+    attention over the whole range.
+    """
+    outs, lses = _f64(outs), _f64(lses)
+    m = np.max(lses, axis=0)
+    safe_m = np.where(np.isfinite(m), m, 0.0)
+    w = np.where(np.isfinite(lses), np.exp(lses - safe_m), 0.0)
+    z = w.sum(axis=0)
+    lse = np.where(z > 0, safe_m + np.log(np.where(z > 0, z, 1.0)), -np.inf)
+    wn = np.where(z > 0, w / np.where(z > 0, z, 1.0), 0.0)
+    out = np.einsum("p...,p...d->...d", wn, np.where(np.isfinite(lses)[..., None], outs, 0.0))
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# cache accounting ([lab] Bloque A)
+# --------------------------------------------------------------------------
+def mha_cache_values_per_token(L, H, d_head):
+    """Standard attention caches K and V per layer and head: 2 L H d_head values per token."""
+    return 2 * L * H * d_head
+
+
+def mla_cache_values_per_token(L, d_c, d_r):
+    """MLA caches c_t and the decoupled rope key: L (d_c + d_r) values per token."""
+    return L * (d_c + d_r)
+
+
+def cache_ratio(H, d_head, d_c, d_r):
+    """M_MHA / M_MLA = 2 H d_head / (d_c + d_r) (the layer count cancels)."""
+    return 2 * H * d_head / (d_c + d_r)
+
+
+# --------------------------------------------------------------------------
+# the RoPE-less notebook ([notebook])
+# --------------------------------------------------------------------------
+def notebook_split_heads(W_uQ, W_uK, W_uV, W_O, h):
+    """Head split of the notebook: [d_c, h*d_h] -> [h, d_c, d_h] by column
+    blocks; W_O [h*d_h, d_model] -> [h, d_h, d_model] by row blocks."""
+    d_c, d_up = np.shape(W_uQ)
+    d_h = d_up // h
+
+    def cols(W):
+        return _f64(W).reshape(d_c, h, d_h).transpose(1, 0, 2)
+
+    return cols(W_uQ), cols(W_uK), cols(W_uV), _f64(W_O).reshape(h, d_h, -1)
+
+
+def notebook_linear_absorbed(X, W_dQ, W_dKV, W_uQ, W_uK, W_uV, W_O, C_KV, h):
+    """The notebook's fully absorbed, softmax-free pipeline.
+
+    W_aQK[h] = W_uQ[h] W_uK[h]^T, W_aVO[h] = W_uV[h] W_O[h]; the new latent
+    X W_dKV is appended to the cache; per head attn = (X W_dQ W_aQK) C^T,
+    out = attn (C W_aVO); final = sum over heads. Returns every array whose
+    shape the notebook prints.
+    """
+    uQ, uK, uV, O = notebook_split_heads(W_uQ, W_uK, W_uV, W_O, h)
+    W_aQK = uQ @ uK.transpose(0, 2, 1)
+    W_aVO = uV @ O
+    C = np.vstack([_f64(C_KV), _f64(X) @ _f64(W_dKV)])
+    C_Q = _f64(X) @ _f64(W_dQ) @ W_aQK
+    attn = C_Q @ C.T
+    score = C @ W_aVO
+    out_heads = attn @ score
+    final = out_heads.sum(axis=0)
+    return dict(X=_f64(X), C_Q=C_Q, C_KV=C, W_aQK=W_aQK, W_aVO=W_aVO, final=final)
+
+
+def notebook_linear_unabsorbed(X, W_dQ, W_dKV, W_uQ, W_uK, W_uV, W_O, C_KV, h):
+    """The same softmax-free computation without absorption: expand q, k, v per
+    head first, then out_h = (q_h k_h^T) v_h W_O[h], summed over heads."""
+    uQ, uK, uV, O = notebook_split_heads(W_uQ, W_uK, W_uV, W_O, h)
+    C = np.vstack([_f64(C_KV), _f64(X) @ _f64(W_dKV)])
+    cq = _f64(X) @ _f64(W_dQ)
+    final = 0.0
+    for s in range(h):
+        q_s, k_s, v_s = cq @ uQ[s], C @ uK[s], C @ uV[s]
+        final = final + (q_s @ k_s.T) @ v_s @ O[s]
+    return final
+
+
+def notebook_softmax_unabsorbed(X, W_dQ, W_dKV, W_uQ, W_uK, W_uV, W_O, C_KV, h, scale):
+    """The notebook's workload with softmax attention, computed unabsorbed.
+
+    Per head: q_h = X W_dQ W_uQ[h], k_t,h = c_t W_uK[h], v_t,h = c_t W_uV[h]
+    over the cache with the new token appended (it attends to itself); the
+    softmax uses `scale`. Returns (v [h, d_h], final [d_model] = sum_h v_h W_O[h]).
+    """
+    uQ, uK, uV, O = notebook_split_heads(W_uQ, W_uK, W_uV, W_O, h)
+    C = np.vstack([_f64(C_KV), _f64(X) @ _f64(W_dKV)])
+    cq = (_f64(X) @ _f64(W_dQ))[0]
+    v = np.zeros((h, uV.shape[2]))
+    final = np.zeros(O.shape[2])
+    for s in range(h):
+        v[s], _ = attend_one_head(cq @ uQ[s], C @ uK[s], C @ uV[s], scale, C.shape[0])
+        final += v[s] @ O[s]
+    return v, final
+
+
+# --------------------------------------------------------------------------
+# gated MLA ([gated]) -- a different variant; used here to pin the
+# single-position behaviour with the page's worked example
+# --------------------------------------------------------------------------
+def gated_mla(x, W_q, W_c, W_k, W_v, W_g, W_o, num_heads, causal):
+    """Gated multi-head latent attention as the tensortonic page states it.
+
+    Q = X W_q^T, C = X W_c^T, K = C W_k^T, V = C W_v^T; per head
+    A = softmax(Q K^T / sqrt(D_h) + M) with M masking later positions when
+    causal; heads concatenated to O~; Y = [sigmoid(X W_g^T) * O~] W_o^T.
+    Returns dict(output [B,S,D], latent_cache [B,S,L]); inputs not modified.
+    """
+    x = _f64(x)
+    B, S, D = x.shape
+    Hn = int(num_heads)
+    Dh = D // Hn
+    Q = x @ _f64(W_q).T
+    C = x @ _f64(W_c).T
+    K = C @ _f64(W_k).T
+    V = C @ _f64(W_v).T
+    Ot = np.zeros((B, S, D))
+    for b in range(B):
+        for hh in range(Hn):
+            sl = slice(hh * Dh, (hh + 1) * Dh)
+            for i in range(S):
+                n = i + 1 if causal else S
+                o, _ = attend_one_head(Q[b, i, sl], K[b, :, sl], V[b, :, sl], 1.0 / math.sqrt(Dh), n)
+                Ot[b, i, sl] = o
+    gate = 1.0 / (1.0 + np.exp(-(x @ _f64(W_g).T)))
+    Y = (gate * Ot) @ _f64(W_o).T
+    return {"output": Y, "latent_cache": C}
