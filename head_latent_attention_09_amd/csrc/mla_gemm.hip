@@ -1,0 +1,249 @@
+// Per-head products around the latent attention, for gfx950.
+//
+//  absorb: q[n,h,j] = sum_i W_UK[h,i,j] q_nope[n,h,i]   (W_UK[h] is [d_nope, d_c];
+//          ferrox-core test, absorbed branch; lab Bloque B; MLA_tutorial q W_qc W_kc^T)
+//          and q[n,h,d_c:] = q_pe[n,h,:]
+//  up_v:   out[n,h,i] = sum_j W_UV[h,i,j] lat[n,h,j]     (W_UV[h] is [d_v, d_c];
+//          ferrox-core module doc v[h] = wv_b[h] . out_lat[h])
+//
+// Both are, per head, C_h = A_h . op(W_h) with A_h the rows [n, h, :] of a
+// [N, H, K] tensor. The bf16 path tiles 128 rows x 128 output columns per
+// workgroup, stages 64-wide K slices of A and W in LDS with direct
+// global->LDS loads (double-buffered), and runs 32x32x16 bf16 MFMA. When W_h
+// is stored [K, D] (absorb) its B-operand fragments come from transposing
+// LDS loads; when stored [D, K] (up_v) they are plain 16-byte LDS reads.
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace gm {
+constexpr int BM = 128, BN = 128, BK = 64, NT = 256;
+constexpr int A_BYTES = BM * BK * 2;  // 16 KiB
+constexpr int B_BYTES = BN * BK * 2;  // 16 KiB
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+
+// rows of 8 chunks (128 B): A tile and [D,K]-stored W tile
+__device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
+// rows of 16 chunks (256 B): [K,D]-stored W tile read by 4-row transposing loads
+__device__ __forceinline__ int swz16(int r) {
+  const int t = r & 3;
+  return t == 0 ? 0 : (t == 1 ? 6 : (t == 2 ? 10 : 12));
+}
+
+struct Args {
+  const bf16* A;   // [N, H, K]
+  const bf16* W;   // TRANS_W: [H, D, K]; else [H, K, D]
+  bf16* out;       // [N, H, ldo], columns 0..D-1 written
+  const bf16* tail_src;  // absorb: q_pe [N, H, tail]; else null
+  int64_t N;
+  int H, K, D, ldo, tail;
+};
+
+__device__ __forceinline__ void wait_all_vm() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <bool TRANS_W>
+__device__ __forceinline__ void issue_stage(const Args& a, char* st, int64_t n0, int h, int j0, int k0, int lane,
+                                            int wv) {
+  // A: 128 rows x 8 chunks = 16 loads of 64 lanes (4 per wave)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ld = wv * 4 + i;
+    const int p = ld * 64 + lane;
+    const int row = p >> 3;
+    const int c = (p & 7) ^ swz8(row);
+    int64_t n = n0 + row;
+    n = n < a.N ? n : a.N - 1;
+    const bf16* src = a.A + ((size_t)n * a.H + h) * a.K + k0 + c * 8;
+    __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(st + ld * 1024), 16, 0, 0);
+  }
+  char* sb = st + A_BYTES;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ld = wv * 4 + i;
+    const int p = ld * 64 + lane;
+    const bf16* src;
+    if (TRANS_W) {  // 128 output columns x 8 chunks along K
+      const int row = p >> 3;
+      const int c = (p & 7) ^ swz8(row);
+      src = a.W + ((size_t)h * a.D + j0 + row) * a.K + k0 + c * 8;
+    } else {        // 64 K rows x 16 chunks along the output columns
+      const int row = p >> 4;
+      const int c = (p & 15) ^ swz16(row);
+      src = a.W + ((size_t)h * a.K + k0 + row) * a.D + j0 + c * 8;
+    }
+    __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(sb + ld * 1024), 16, 0, 0);
+  }
+}
+
+template <bool TRANS_W>
+__global__ __launch_bounds__(NT, 2) void gemm_mfma_kernel(Args a) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = lane >> 5;
+  const int64_t n0 = (int64_t)blockIdx.x * BM;
+  const int j0 = blockIdx.y * BN;
+  const int h = blockIdx.z;
+  const int wm = wv >> 1, wn = wv & 1;  // wave tile: rows wm*64.., cols wn*64..
+  const int nk = a.K / BK;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  issue_stage<TRANS_W>(a, smem, n0, h, j0, 0, lane, wv);
+  for (int kc = 0; kc < nk; ++kc) {
+    wait_all_vm();
+    barrier();
+    if (kc + 1 < nk) issue_stage<TRANS_W>(a, smem + ((kc + 1) & 1) * STAGE_BYTES, n0, h, j0, (kc + 1) * BK, lane, wv);
+    const char* sa = smem + (kc & 1) * STAGE_BYTES;
+    const char* sb = sa + A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = wm * 64 + i * 32 + (lane & 31);
+        af[i] = *(const MLA_LDS bf16x8*)(sa + row * 128 + (((2 * ks + g) ^ swz8(row)) * 16));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (TRANS_W) {
+          const int row = wn * 64 + j * 32 + (lane & 31);
+          bfr[j] = *(const MLA_LDS bf16x8*)(sb + row * 128 + (((2 * ks + g) ^ swz8(row)) * 16));
+        } else {
+          // B lane: output column wn*64 + j*32 + lane%32, K slots 16ks + 8g + 0..7;
+          // 16-lane group reads 4 K-rows x 16 columns per transposing load.
+          const int q16 = lane & 15, hf = (lane >> 4) & 1;
+          const int krow = 16 * ks + 8 * g + (q16 >> 2);
+          const int c = (wn * 64 + j * 32 + 16 * hf + (q16 & 3) * 4) >> 3;
+          const char* pa = sb + krow * 256 + ((c ^ swz16(krow)) * 16) + (q16 & 1) * 8;
+          const char* pb = sb + (krow + 4) * 256 + ((c ^ swz16(krow + 4)) * 16) + (q16 & 1) * 8;
+          s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)pa);
+          s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)pb);
+          typedef short s16x8 __attribute__((ext_vector_type(8)));
+          s16x8 v8 = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+          bfr[j] = __builtin_bit_cast(bf16x8, v8);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  // D layout: lane column = lane%32, rows 8(r/4) + 4g + r%4
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = j0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t n = n0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (n < a.N) a.out[((size_t)n * a.H + h) * a.ldo + col] = f32_to_bf16(acc[i][j][r]);
+      }
+    }
+  // absorb: copy q_pe into the tail of the query rows (once per row block)
+  if (a.tail_src && blockIdx.y == 0) {
+    for (int idx = threadIdx.x; idx < BM * a.tail; idx += NT) {
+      const int row = idx / a.tail, k = idx - row * a.tail;
+      const int64_t n = n0 + row;
+      if (n < a.N) a.out[((size_t)n * a.H + h) * a.ldo + a.D + k] = a.tail_src[((size_t)n * a.H + h) * a.tail + k];
+    }
+  }
+}
+}  // namespace gm
+
+// generic per-head product: one thread per output element, fp32 accumulation
+template <typename T, bool TRANS_W>
+__global__ __launch_bounds__(256) void gemm_generic_kernel(const T* A, const T* W, T* out, int64_t N, int H, int K,
+                                                           int D, int ldo) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = N * H * (int64_t)D;
+  if (idx >= total) return;
+  const int i = (int)(idx % D);
+  const int64_t nh = idx / D;
+  const int h = (int)(nh % H);
+  const T* a = A + nh * K;
+  float acc = 0.f;
+  if (TRANS_W) {
+    const T* w = W + ((size_t)h * D + i) * K;
+    for (int k = 0; k < K; ++k) acc += load_f32(a + k) * load_f32(w + k);
+  } else {
+    const T* w = W + (size_t)h * K * D + i;
+    for (int k = 0; k < K; ++k) acc += load_f32(a + k) * load_f32(w + (size_t)k * D);
+  }
+  store_f32(out + nh * ldo + i, acc);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void copy_tail_kernel(const T* src, T* out, int64_t rows, int tail, int ldo,
+                                                        int col0) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * tail) return;
+  const int64_t row = idx / tail;
+  const int k = (int)(idx - row * tail);
+  out[row * ldo + col0 + k] = src[idx];
+}
+
+static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+template <typename T, bool TRANS_W>
+static int run_generic(const void* A, const void* W, void* out, int64_t N, int H, int K, int D, int ldo,
+                       hipStream_t s) {
+  const int64_t total = N * H * (int64_t)D;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > 0)
+    hipLaunchKernelGGL((gemm_generic_kernel<T, TRANS_W>), dim3((unsigned)blocks), dim3(256), 0, s, (const T*)A,
+                       (const T*)W, (T*)out, N, H, K, D, ldo);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+static bool mfma_ok(int K, int D, int ldo, const void* A, const void* W, const void* out) {
+  return K % gm::BK == 0 && D % gm::BN == 0 && ldo % 8 == 0 && al16(A) && al16(W) && al16(out);
+}
+
+int launch_absorb(const void* q_nope, const void* q_pe, const void* w_uk, void* q, int64_t N, int H, int d_nope,
+                  int d_c, int d_r, int dtype, hipStream_t s) {
+  const int ldo = d_c + d_r;
+  if (dtype == MLA_BF16 && mfma_ok(d_nope, d_c, ldo, q_nope, w_uk, q)) {
+    gm::Args a{(const bf16*)q_nope, (const bf16*)w_uk, (bf16*)q, d_r > 0 ? (const bf16*)q_pe : nullptr,
+               N, H, d_nope, d_c, ldo, d_r};
+    dim3 grid((unsigned)((N + gm::BM - 1) / gm::BM), d_c / gm::BN, H);
+    hipLaunchKernelGGL(gm::gemm_mfma_kernel<false>, grid, dim3(gm::NT), 0, s, a);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  }
+  int st = dtype == MLA_BF16 ? run_generic<bf16, false>(q_nope, w_uk, q, N, H, d_nope, d_c, ldo, s)
+                             : run_generic<float, false>(q_nope, w_uk, q, N, H, d_nope, d_c, ldo, s);
+  if (st != MLA_OK || d_r == 0) return st;
+  const int64_t rows = N * H;
+  const int64_t blocks = (rows * d_r + 255) / 256;
+  if (dtype == MLA_BF16)
+    hipLaunchKernelGGL(copy_tail_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, s, (const bf16*)q_pe, (bf16*)q,
+                       rows, d_r, ldo, d_c);
+  else
+    hipLaunchKernelGGL(copy_tail_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, (const float*)q_pe,
+                       (float*)q, rows, d_r, ldo, d_c);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int launch_up_v(const void* lat, const void* w_uv, void* out, int64_t N, int H, int d_c, int d_v, int dtype,
+                hipStream_t s) {
+  if (dtype == MLA_BF16 && mfma_ok(d_c, d_v, d_v, lat, w_uv, out)) {
+    gm::Args a{(const bf16*)lat, (const bf16*)w_uv, (bf16*)out, nullptr, N, H, d_c, d_v, d_v, 0};
+    dim3 grid((unsigned)((N + gm::BM - 1) / gm::BM), d_v / gm::BN, H);
+    hipLaunchKernelGGL(gm::gemm_mfma_kernel<true>, grid, dim3(gm::NT), 0, s, a);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  }
+  return dtype == MLA_BF16 ? run_generic<bf16, true>(lat, w_uv, out, N, H, d_c, d_v, d_v, s)
+                           : run_generic<float, true>(lat, w_uv, out, N, H, d_c, d_v, d_v, s);
+}
+
+}  // namespace mla

@@ -1,0 +1,156 @@
+// Internal declarations of libmla: device helpers and kernel launchers.
+// Target: gfx950 (CDNA4) only; 64-lane wavefronts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "mla.h"
+
+namespace mla {
+
+// ---------------------------------------------------------------------------
+// vector types used as MFMA operands
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ bf16 f32_to_bf16(float x) { return (bf16)x; }  // nearest-even (v_cvt_pk_bf16_f32)
+
+template <typename T> __device__ __forceinline__ float load_f32(const T* p);
+template <> __device__ __forceinline__ float load_f32<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load_f32<bf16>(const bf16* p) { return (float)*p; }
+template <typename T> __device__ __forceinline__ void store_f32(T* p, float v);
+template <> __device__ __forceinline__ void store_f32<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void store_f32<bf16>(bf16* p, float v) { *p = (bf16)v; }
+
+// ---------------------------------------------------------------------------
+// split-sequence plan shared by the attention kernels and the combine.
+//
+// The work of a call is a list of R "rows" (decode: one per sequence;
+// prefill: one per query), each with len[r] visible positions cut into
+// tiles of TILE positions. Tiles of all rows are concatenated in row order
+// and dealt out in equal contiguous ranges of `per_worker` tiles to G
+// workers (one workgroup each). A worker's range is a run of segments, one
+// per row it touches. A row entirely inside one worker is finished by that
+// worker; a row cut by worker boundaries leaves one fp32 partial result
+// (normalised output + lse) per touching worker, merged by the combine.
+// Partial slot of (worker w, row r): 2w if r started before w's range
+// (r is w's first segment), else 2w + 1 (r runs past w's end). So 2G slots.
+// ---------------------------------------------------------------------------
+struct Plan {
+  int32_t* cum;     // [R + 1]: exclusive prefix sum of tiles per row (cum[R] = total)
+  int32_t* len;     // [R]: visible positions per row (clamped)
+  int32_t* flags;   // [R]: set when a row must be recomputed by the generic kernel
+  float* part_o;    // [2G, H, d_c]
+  float* part_lse;  // [2G, H]
+  int R;
+  int G;
+  int tile;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// workspace layout: cum | len | flags | part_o | part_lse
+inline size_t plan_bytes(int64_t R, int G, int H, int d_c) {
+  size_t b = align256(sizeof(int32_t) * (size_t)(R + 1));
+  b += 2 * align256(sizeof(int32_t) * (size_t)R);
+  b += align256(sizeof(float) * (size_t)2 * G * H * d_c);
+  b += align256(sizeof(float) * (size_t)2 * G * H);
+  return b;
+}
+
+inline Plan plan_layout(void* ws, int R, int G, int H, int d_c, int tile) {
+  char* p = (char*)ws;
+  Plan pl;
+  pl.cum = (int32_t*)p;
+  p += align256(sizeof(int32_t) * (size_t)(R + 1));
+  pl.len = (int32_t*)p;
+  p += align256(sizeof(int32_t) * (size_t)R);
+  pl.flags = (int32_t*)p;
+  p += align256(sizeof(int32_t) * (size_t)R);
+  pl.part_o = (float*)p;
+  p += align256(sizeof(float) * (size_t)2 * G * H * d_c);
+  pl.part_lse = (float*)p;
+  pl.R = R;
+  pl.G = G;
+  pl.tile = tile;
+  return pl;
+}
+
+__device__ __forceinline__ int plan_per_worker(int total, int G) {
+  int q = (total + G - 1) / G;
+  return q < 1 ? 1 : q;
+}
+
+// Worker index of this workgroup. Workgroups are dispatched round-robin over
+// the 8 XCDs (blockIdx.x % 8); consecutive workers share rows (and the
+// query rows they re-read), so place consecutive workers on the same XCD.
+__device__ __forceinline__ int xcd_worker(int bx, int G) {
+  if (G % 8 != 0) return bx;
+  return (bx % 8) * (G / 8) + bx / 8;
+}
+
+// first row whose tiles contain global tile t (cum[row] <= t < cum[row+1])
+__device__ __forceinline__ int plan_row_of(const int32_t* cum, int R, int t) {
+  int lo = 0, hi = R - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cum[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int plan_slot(int w, int row_start_tile, int per_worker) {
+  return (row_start_tile < w * per_worker) ? 2 * w : 2 * w + 1;
+}
+
+// description of where row r's query, cache and output live
+struct RowMap {
+  int mode;            // 0 = decode dense, 1 = decode paged, 2 = prefill
+  int s_q, s_kv;       // prefill
+  int cache_stride;    // dense rows per sequence
+  int page_size, max_pages, num_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+};
+
+// ---------------------------------------------------------------------------
+// launchers (mla_attn.hip / mla_gemm.hip)
+// ---------------------------------------------------------------------------
+struct AttnCall {
+  const void* q;
+  const void* cache;
+  RowMap map;
+  int R, H, d_c, d_r;
+  float kq_scale;
+  int dtype;
+  void* out;
+  float* lse;
+  void* ws;
+  int G;
+  void* const* timing_events;
+  hipStream_t stream;
+};
+
+int attn_tile_size(const AttnCall& c);          // tile used by the kernel path chosen for c
+int launch_attention(const AttnCall& c);        // plan + attention + combine
+int launch_lse_combine(const float* o_parts, const float* lse_parts, int n_parts, int64_t rows,
+                       int H, int d_c, int dtype, void* out, float* lse, hipStream_t stream);
+int launch_absorb(const void* q_nope, const void* q_pe, const void* w_uk, void* q, int64_t N,
+                  int H, int d_nope, int d_c, int d_r, int dtype, hipStream_t stream);
+int launch_up_v(const void* lat, const void* w_uv, void* out, int64_t N, int H, int d_c,
+                int d_v, int dtype, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,185 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) weight-absorbed Multi-head Latent
+ * Attention library (libmla.so).
+ *
+ * What it computes (notation of the pages this library follows):
+ *   The cache holds one row per position, [c_t | k_pe_t]: the RMS-normed
+ *   latent c_t (d_c wide) followed by the roped rope key k_pe_t (d_r wide)
+ *   (docs.rs ferrox-core 0.23.0, src/mla_absorbed.rs: documentation of
+ *   `causal_mla_absorbed_attention`, llama.cpp's concat(kv_cmpr, k_pe) order).
+ *   A query row is [q_abs | q_pe] with q_abs = W_UK[h]^T q_nope[h] (same page,
+ *   module documentation; MLA_tutorial formula.md Part 3, inference form).
+ *   Every head scores against the SAME key row and sums the SAME value c_t:
+ *     score[h][t] = (q_abs[h].c_t + q_pe[h].k_pe_t) * kq_scale
+ *     out_lat[h]  = sum_t softmax_t(score[h]) c_t         (d_c wide)
+ *     v[h]        = W_UV[h] out_lat[h]                     (d_v wide)
+ *   kq_scale is the caller's 1/sqrt(d_nope + d_r): the width of the
+ *   unabsorbed head, never the latent width (ferrox-core module doc).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers to caller-owned memory, row-major
+ *     and contiguous in the innermost dimension. The library never
+ *     allocates, frees or synchronises the host in these calls; scratch for
+ *     split-sequence partial results comes from the caller's workspace.
+ *   - Inputs are never written (the gated-MLA problem statement's "do not
+ *     mutate any input tensor"); every element of every output is written.
+ *   - All tensors of one call share `dtype` (MLA_F32 or MLA_BF16);
+ *     accumulation is fp32; outputs are in `dtype`; lse outputs are fp32.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs asynchronously. Calls keep no state between them apart from
+ *     a cached per-device compute-unit count.
+ *   - Errors are returned as negative status codes BEFORE any launch for
+ *     argument problems; MLA_ERR_HIP reports a failed launch. A call that
+ *     returns an error has enqueued nothing, except MLA_ERR_HIP, after which
+ *     the state of the outputs is unspecified.
+ *   - Size arguments of value 0 in a batch-like dimension (tokens, batch,
+ *     query rows) are valid and do nothing.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  MLA_ERR_SHAPE = -2,       /* a size is negative, zero where it must be positive,
+                               or sizes are inconsistent with each other          */
+  MLA_ERR_DTYPE = -3,       /* dtype is neither MLA_F32 nor MLA_BF16              */
+  MLA_ERR_UNSUPPORTED = -4, /* sizes beyond the library's limits (see each call)  */
+  MLA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the query returns   */
+  MLA_ERR_ALIGN = -6,       /* a pointer not aligned to its element size          */
+  MLA_ERR_SCALE = -7,       /* kq_scale is not a finite number                    */
+  MLA_ERR_HIP = -8          /* a HIP runtime call or kernel launch failed          */
+};
+
+/* Text for a status code (static storage; never NULL). */
+const char* mla_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int mla_version(void);
+
+/* Default worker count used when num_workers == 0: the compute-unit count of
+ * the current HIP device (one attention workgroup per compute unit).
+ * Returns a negative status if no device is available. */
+int mla_default_workers(void);
+
+/* ---------------------------------------------------------------------------
+ * Query absorption (ferrox-core test, absorbed branch: the query pushed
+ * through k_b; lab "MLA math exercise" Bloque B identity
+ * q^T W_UK c = (W_UK^T q)^T c; MLA_tutorial inference form q W_qc W_kc^T):
+ *   q[n,h,j]       = sum_i W_UK[h,i,j] * q_nope[n,h,i]   for j < d_c
+ *   q[n,h,d_c + k] = q_pe[n,h,k]                         for k < d_r
+ * q_nope [n_tokens, n_heads, d_nope]; q_pe [n_tokens, n_heads, d_r] (may be
+ * NULL only when d_r == 0); w_uk [n_heads, d_nope, d_c] (the k_b rows of
+ * kv_b); q [n_tokens, n_heads, d_c + d_r] (output).
+ * Limits: n_heads <= 65535, d_nope, d_c <= 4096, d_r <= 1024.
+ * ------------------------------------------------------------------------- */
+int mla_absorb_q(const void* q_nope, const void* q_pe, const void* w_uk, void* q,
+                 int64_t n_tokens, int n_heads, int d_nope, int d_c, int d_r,
+                 int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Value up-projection after the latent attention (ferrox-core module doc
+ * v[h] = wv_b[h] . out_lat[h]; MLA_tutorial inference form o^(s) W_v^(s)):
+ *   out[n,h,i] = sum_j W_UV[h,i,j] * out_lat[n,h,j]
+ * out_lat [n_tokens, n_heads, d_c]; w_uv [n_heads, d_v, d_c] (the v_b rows
+ * of kv_b); out [n_tokens, n_heads, d_v].
+ * Limits: n_heads <= 65535, d_c, d_v <= 4096.
+ * ------------------------------------------------------------------------- */
+int mla_up_v(const void* out_lat, const void* w_uv, void* out,
+             int64_t n_tokens, int n_heads, int d_c, int d_v, int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Absorbed decode: one query token per sequence attends to its sequence's
+ * latent cache (ferrox-core `causal_mla_absorbed_attention`, generalised to
+ * a batch, a dense or paged cache and split-sequence execution).
+ *   q            [batch, n_heads, d_c + d_r]  rows [q_abs | q_pe]
+ *   latent_cache dense (block_table == NULL): [batch, cache_stride, d_c + d_r];
+ *                paged: a pool [num_pages, page_size, d_c + d_r]
+ *   seq_lens     [batch] int32, DEVICE memory: positions 0..len-1 attend.
+ *                Values are clamped to [0, cache_stride] (dense) or
+ *                [0, max_pages * page_size] (paged) before use.
+ *   block_table  [batch, max_pages] int32, DEVICE memory, or NULL for dense.
+ *                Entry (b, j) is the pool page of positions j*page_size ..;
+ *                entries are clamped to [0, num_pages - 1] before use.
+ *   out_lat      [batch, n_heads, d_c] output (the weighted sum of c_t, before W_UV)
+ *   lse          [batch, n_heads] fp32 output (natural-log softmax
+ *                normaliser, max included), or NULL.
+ * A sequence of length 0 yields out_lat = 0 and lse = -inf (the empty-sum
+ * guard of `causal_mla_absorbed_attention`).
+ * workspace / workspace_bytes: device scratch of at least
+ *   mla_latent_decode_workspace(batch, n_heads, d_c, num_workers) bytes;
+ *   contents on entry are ignored. Concurrent calls need separate workspaces.
+ * num_workers: attention workgroups to launch (0 = mla_default_workers()).
+ *   Results do not depend on it beyond floating-point rounding.
+ * timing_events: NULL, or a pointer to two hipEvent_t that are recorded on
+ *   `stream` immediately before and after the attention kernel (for
+ *   profiling; the planning and combine kernels fall outside them).
+ * Limits: d_c <= 1024, d_c + d_r <= 1152, n_heads <= 65535,
+ *   page_size >= 1 when paged.
+ * ------------------------------------------------------------------------- */
+size_t mla_latent_decode_workspace(int batch, int n_heads, int d_c, int num_workers);
+
+int mla_latent_decode(const void* q, const void* latent_cache,
+                      const int32_t* seq_lens, const int32_t* block_table,
+                      int batch, int n_heads, int d_c, int d_r,
+                      int cache_stride, int page_size, int max_pages, int num_pages,
+                      float kq_scale, int dtype,
+                      void* out_lat, float* lse,
+                      void* workspace, size_t workspace_bytes,
+                      int num_workers, void* const* timing_events, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Causal prefill over the latent cache: every query of a chunk attends to
+ * the cache positions the causal mask leaves visible (gated-MLA statement:
+ * later positions are masked before the softmax, diagonal included;
+ * MLA_tutorial: sums over i <= t). Alignment is bottom-right: query i
+ * (0-based, of s_q) sees positions t <= i + s_kv - s_q.
+ *   q            [batch, s_q, n_heads, d_c + d_r]
+ *   latent_cache [batch, s_kv, d_c + d_r]
+ *   out_lat      [batch, s_q, n_heads, d_c]; lse [batch, s_q, n_heads] or NULL.
+ * Queries that see no position (s_q > s_kv) get zeros and lse = -inf.
+ * workspace: at least mla_latent_prefill_causal_workspace(batch, s_q,
+ *   n_heads, d_c, num_workers) bytes. num_workers, timing_events: as decode.
+ * Limits: as decode; batch * s_q <= 2^31 - 1.
+ * ------------------------------------------------------------------------- */
+size_t mla_latent_prefill_causal_workspace(int batch, int s_q, int n_heads, int d_c, int num_workers);
+
+int mla_latent_prefill_causal(const void* q, const void* latent_cache,
+                              int batch, int s_q, int s_kv, int n_heads, int d_c, int d_r,
+                              float kq_scale, int dtype,
+                              void* out_lat, float* lse,
+                              void* workspace, size_t workspace_bytes,
+                              int num_workers, void* const* timing_events, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Log-sum-exp merge of softmax results computed over disjoint position
+ * ranges of the same queries (the split-sequence combine step; it is the
+ * identity softmax over a union of ranges satisfies, not a formula of the
+ * pages):
+ *   lse[r,h]   = log sum_p exp(lse_parts[p,r,h])
+ *   out[r,h,:] = sum_p exp(lse_parts[p,r,h] - lse[r,h]) * o_parts[p,r,h,:]
+ * o_parts [n_parts, rows, n_heads, d_c] fp32, each normalised over its own
+ * range; lse_parts [n_parts, rows, n_heads] fp32. Parts with lse = -inf
+ * (empty ranges) are skipped and their o_parts values never read; if all
+ * are -inf the output is 0 and lse -inf. out [rows, n_heads, d_c] in
+ * `dtype`; lse [rows, n_heads] fp32 or NULL.
+ * Limits: 1 <= n_parts <= 4096, d_c <= 4096, n_heads <= 65535.
+ * ------------------------------------------------------------------------- */
+int mla_lse_combine(const float* o_parts, const float* lse_parts, int n_parts,
+                    int64_t rows, int n_heads, int d_c, int dtype,
+                    void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

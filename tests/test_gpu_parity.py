@@ -1,0 +1,342 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Same seeded inputs on both sides; small cases are compared element by element,
+full-size workloads on sampled outputs the oracle computes one by one.
+Bar: max|gpu - oracle| / max|oracle| <= 1e-4 (fp32) or 2e-2 (bf16 inputs,
+fp32 accumulation); lse within the same bound in absolute terms.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as G
+from gpu_util import LSE_TOL, TOL, dtype_torch, lse_err, rel_err, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+M = None
+
+
+def setup_module(module):
+    global M
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import head_latent_attention_09_amd as lib_mod
+    M = lib_mod
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+def run_decode(case, num_workers=0):
+    q = to_dev(case.q, case.dtype)
+    lens = torch.from_numpy(case.lens.astype(np.int32)).cuda()
+    if case.page_size is None:
+        cache = to_dev(case.cache, case.dtype)
+        out, lse = M.latent_decode(q, cache, lens, case.d_c, case.kq_scale, num_workers=num_workers)
+    else:
+        cache = to_dev(case.pages, case.dtype)
+        table = torch.from_numpy(case.block_table).cuda()
+        out, lse = M.latent_decode(q, cache, lens, case.d_c, case.kq_scale, block_table=table,
+                                   num_workers=num_workers)
+    torch.cuda.synchronize()
+    return to_host64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_decode(case, rows=None, heads=None):
+    rows = range(case.B) if rows is None else rows
+    outs, lses = [], []
+    for b in rows:
+        lat = G.to_f64(G.seq_rows(case, b), case.dtype)
+        q = G.to_f64(case.q[b], case.dtype)
+        o, l = O.latent_attention(q, lat, case.d_c, case.kq_scale, int(case.lens[b]), heads)
+        outs.append(o)
+        lses.append(l)
+    return np.array(outs), np.array(lses)
+
+
+def check_decode(case, num_workers=0, label=""):
+    say(f"decode {label}: dtype={case.dtype} B={case.B} H={case.H} d_c={case.d_c} d_r={case.d_r} "
+        f"lens={list(case.lens)[:8]} paged={case.page_size} workers={num_workers}")
+    got, glse = run_decode(case, num_workers)
+    ref, rlse = oracle_decode(case)
+    e, le = rel_err(got, ref), lse_err(glse, rlse)
+    say(f"  out rel err {e:.3e}  lse abs err {le:.3e}")
+    assert e <= TOL[case.dtype] and le <= LSE_TOL[case.dtype]
+    return got, glse
+
+
+@pytest.mark.parametrize("dtype", [G.BF16, G.F32])
+@pytest.mark.parametrize("H", [128, 64, 16])
+def test_decode_dense_small(dtype, H):
+    lens = [1, 45, 100, 0, 257]
+    case = G.decode_case(5, H, 512, 64, lens, dtype, seed=100 + H, cache_rows=300)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    check_decode(case, label="dense small")
+
+
+@pytest.mark.parametrize("workers", [1, 3, 7, 64, 0])
+def test_decode_split_count_invariance(workers):
+    case = G.decode_case(3, 128, 512, 64, [700, 33, 1000], G.BF16, seed=7)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    check_decode(case, num_workers=workers, label="split invariance")
+
+
+@pytest.mark.parametrize("dtype", [G.BF16, G.F32])
+def test_decode_paged_small(dtype):
+    lens = [64, 1, 130, 0, 200, 65]
+    case = G.decode_case(6, 128, 512, 64, lens, dtype, seed=31, page_size=64)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    check_decode(case, num_workers=16, label="paged small")
+
+
+def test_decode_odd_shapes_generic():
+    """d_c, d_r, H outside the MFMA specialisation (generic kernel), bf16 and fp32."""
+    for dtype in (G.BF16, G.F32):
+        case = G.decode_case(3, 5, 96, 32, [17, 50, 3], dtype, seed=5)
+        case.kq_scale = 0.2
+        check_decode(case, num_workers=5, label="odd shapes")
+
+
+def test_decode_single_position_is_latent_row():
+    """One visible position: softmax weight 1, output = c_0 exactly (bf16)."""
+    case = G.decode_case(4, 128, 512, 64, [1, 1, 1, 1], G.BF16, seed=9)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    got, glse = run_decode(case)
+    for b in range(4):
+        c0 = G.to_f64(G.seq_rows(case, b), G.BF16)[0, :512]
+        assert np.array_equal(got[b], np.broadcast_to(c0, got[b].shape))
+
+
+def test_decode_zero_query_is_mean():
+    case = G.decode_case(2, 128, 512, 64, [300, 77], G.BF16, seed=12)
+    case.q[:] = 0
+    case.kq_scale = 1.0 / math.sqrt(192)
+    got, glse = run_decode(case)
+    for b in range(2):
+        lat = G.to_f64(G.seq_rows(case, b), G.BF16)
+        mean = lat[:, :512].mean(axis=0)
+        assert rel_err(got[b], np.broadcast_to(mean, got[b].shape)) <= 2e-2
+        assert np.allclose(glse[b], math.log(case.lens[b]), atol=1e-3)
+
+
+def test_decode_large_logits_fixup():
+    """Scores that rise by far more than 2^32 within a sequence (handled by the
+    recompute path of rows whose fixed softmax reference overflowed)."""
+    case = G.decode_case(2, 128, 512, 64, [600, 300], G.BF16, seed=13)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    cache = G.to_f64(case.cache, G.BF16)
+    ramp = np.linspace(0.0, 60.0, cache.shape[1])
+    cache[:, :, 512] = ramp[None, :]          # one rope coordinate grows along the sequence
+    case.cache = G.storage(cache, G.BF16)
+    q = G.to_f64(case.q, G.BF16)
+    q[:, :, 512] = 40.0
+    case.q = G.storage(q, G.BF16)
+    check_decode(case, num_workers=4, label="large logits")
+
+
+# ----------------------------------------------------------------------------
+# full-size workloads
+# ----------------------------------------------------------------------------
+def test_config2_full_fp32():
+    case = G.config2_decode_f32(0)
+    check_decode(case, label="config 2")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_config3_sampled():
+    case = G.config3_decode_bf16(0)
+    say("config 3: generating done; running decode + up_v")
+    q = to_dev(case.q, G.BF16)
+    cache = to_dev(case.cache, G.BF16)
+    lens = torch.from_numpy(case.lens).cuda()
+    w_uv = to_dev(case.w_uv, G.BF16)
+    out_lat, lse = M.latent_decode(q, cache, lens, 512, case.kq_scale)
+    v = M.up_v(out_lat, w_uv)
+    torch.cuda.synchronize()
+    out_lat, v, lse = to_host64(out_lat), to_host64(v), lse.cpu().numpy()
+    rng = np.random.default_rng(3)
+    samples = [(0, 0), (63, 127)] + [tuple(x) for x in zip(rng.integers(0, 64, 6), rng.integers(0, 128, 6))]
+    wuv = G.to_f64(case.w_uv, G.BF16)
+    for b, h in samples:
+        lat = G.to_f64(case.cache[b], G.BF16)
+        qb = G.to_f64(case.q[b], G.BF16)
+        ro, rl = O.latent_attention(qb, lat, 512, case.kq_scale, 4096, [h])
+        rv, _ = O.latent_attention_expanded_v(qb, lat, 512, wuv, case.kq_scale, 4096, [h])
+        e1, e2, e3 = rel_err(out_lat[b, h], ro[0]), rel_err(v[b, h], rv[0]), abs(lse[b, h] - rl[0])
+        say(f"  (b={b}, h={h}) out_lat {e1:.2e} v {e2:.2e} lse {e3:.2e}")
+        assert e1 <= 2e-2 and e2 <= 2e-2 and e3 <= 2e-2
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_config4_sampled():
+    case = G.config4_paged_bf16(0)
+    say(f"config 4: {int(case.lens.sum())} tokens in {case.pages.shape[0]} pages")
+    got, glse = run_decode(case)
+    order = np.argsort(case.lens)
+    rows = sorted(set([int(order[0]), int(order[-1]), int(order[64])] + list(range(0, 128, 41))))
+    ref, rlse = oracle_decode(case, rows=rows)
+    for i, b in enumerate(rows):
+        e, le = rel_err(got[b], ref[i]), lse_err(glse[b], rlse[i])
+        say(f"  seq {b} len {case.lens[b]}: out {e:.2e} lse {le:.2e}")
+        assert e <= 2e-2 and le <= 2e-2
+
+
+# ----------------------------------------------------------------------------
+# causal prefill, absorb, up_v
+# ----------------------------------------------------------------------------
+def run_prefill_chain(case, num_workers=0):
+    qn, qp = to_dev(case.q_nope, case.dtype), to_dev(case.q_pe, case.dtype)
+    wuk, wuv = to_dev(case.w_uk, case.dtype), to_dev(case.w_uv, case.dtype)
+    cache = to_dev(case.cache, case.dtype)
+    B, S, H = case.B, case.S_q, case.H
+    q = M.absorb_q(qn.reshape(B * S, H, -1), qp.reshape(B * S, H, -1), wuk)
+    out_lat, lse = M.latent_prefill_causal(q.reshape(B, S, H, -1), cache, case.d_c, case.kq_scale,
+                                           num_workers=num_workers)
+    v = M.up_v(out_lat.reshape(B * S, H, -1), wuv)
+    torch.cuda.synchronize()
+    return (to_host64(q).reshape(B, S, H, -1), to_host64(out_lat), lse.cpu().numpy(),
+            to_host64(v).reshape(B, S, H, -1))
+
+
+@pytest.mark.parametrize("dtype,H,d_c,d_r,d_nope,d_v,S_q,S_kv", [
+    (G.BF16, 128, 512, 64, 128, 128, 70, 70),     # MFMA path, several tiles, ragged tail
+    (G.BF16, 128, 512, 64, 128, 128, 40, 100),    # chunk at the end of a longer cache
+    (G.F32, 8, 64, 16, 32, 24, 33, 33),           # generic path
+    (G.BF16, 32, 512, 64, 128, 128, 50, 20),      # more queries than cache rows
+])
+def test_prefill_chain_small(dtype, H, d_c, d_r, d_nope, d_v, S_q, S_kv):
+    say(f"prefill chain: {dtype} H={H} d_c={d_c} S_q={S_q} S_kv={S_kv}")
+    case = G.prefill_case(2, S_q, S_kv, H, d_nope, d_c, d_r, d_v, dtype, seed=21)
+    gq, gout, glse, gv = run_prefill_chain(case, num_workers=13)
+    tol = TOL[dtype]
+    for b in range(case.B):
+        qn, qp = G.to_f64(case.q_nope[b], dtype), G.to_f64(case.q_pe[b], dtype)
+        wuk, wuv = G.to_f64(case.w_uk, dtype), G.to_f64(case.w_uv, dtype)
+        rq = O.absorb_query(qn, qp, wuk)
+        assert rel_err(gq[b], rq) <= tol
+        lat = G.to_f64(case.cache[b], dtype)
+        ro, rl = O.latent_prefill_causal(rq, lat, d_c, case.kq_scale)
+        e, le = rel_err(gout[b], ro), lse_err(glse[b], rl)
+        # end to end against the unabsorbed definition (per-head expanded K and V)
+        ev = 0.0
+        for i in range(0, S_q, max(1, S_q // 7)):
+            n = O.causal_visible(i, S_q, S_kv)
+            rv, _ = O.mla_unabsorbed(qn[i], qp[i], lat, d_c, wuk, wuv, case.kq_scale, n)
+            ev = max(ev, rel_err(gv[b, i], rv))
+        say(f"  b={b}: out {e:.2e} lse {le:.2e} v(unabsorbed) {ev:.2e}")
+        assert e <= tol and le <= LSE_TOL[dtype] and ev <= tol
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_config5_sampled():
+    case = G.config5_prefill_bf16(0)
+    say("config 5 generated; running absorb + prefill + up_v")
+    gq, gout, glse, gv = run_prefill_chain(case)
+    wuk, wuv = G.to_f64(case.w_uk, G.BF16), G.to_f64(case.w_uv, G.BF16)
+    for b in range(2):
+        lat = G.to_f64(case.cache[b], G.BF16)
+        for i in [0, 1, 31, 32, 1000, 4095]:
+            qn, qp = G.to_f64(case.q_nope[b, i], G.BF16), G.to_f64(case.q_pe[b, i], G.BF16)
+            rq = O.absorb_query(qn, qp, wuk)
+            eq = rel_err(gq[b, i], rq)
+            ro, rl = O.latent_attention(rq, lat, 512, case.kq_scale, i + 1)
+            e, le = rel_err(gout[b, i], ro), lse_err(glse[b, i], rl)
+            hs = [0, 77, 127]
+            rv = np.array([O.mla_unabsorbed(qn[[h]], qp[[h]], lat, 512, wuk[[h]], wuv[[h]], case.kq_scale,
+                                            i + 1)[0][0] for h in hs])
+            ev = rel_err(gv[b, i, hs], rv)
+            say(f"  b={b} i={i}: q {eq:.2e} out {e:.2e} lse {le:.2e} v {ev:.2e}")
+            assert eq <= 2e-2 and e <= 2e-2 and le <= 2e-2 and ev <= 2e-2
+
+
+@pytest.mark.parametrize("dtype,N,H,d_in,d_out", [
+    (G.BF16, 300, 4, 512, 128), (G.BF16, 64, 128, 512, 128), (G.F32, 5, 3, 20, 20), (G.BF16, 7, 2, 40, 24)])
+def test_up_v(dtype, N, H, d_in, d_out):
+    say(f"up_v {dtype} N={N} H={H} {d_in}->{d_out}")
+    c = G.gemm_case(N, H, d_in, d_out, dtype, seed=N, transpose_w=True)
+    got = to_host64(M.up_v(to_dev(c.x, dtype), to_dev(c.w, dtype)))
+    ref = O.up_project(G.to_f64(c.x, dtype), G.to_f64(c.w, dtype))
+    assert rel_err(got, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,N,H,d_nope,d_c,d_r", [
+    (G.BF16, 300, 4, 128, 512, 64), (G.BF16, 129, 2, 64, 256, 0), (G.F32, 3, 3, 20, 20, 0), (G.F32, 9, 2, 4, 6, 2)])
+def test_absorb(dtype, N, H, d_nope, d_c, d_r):
+    say(f"absorb {dtype} N={N} H={H} {d_nope}->{d_c} + {d_r}")
+    c = G.gemm_case(N, H, d_nope, d_c, dtype, seed=N + 1, transpose_w=False)
+    qp = G.storage(np.random.default_rng(N).standard_normal((N, H, d_r)), dtype)
+    got = to_host64(M.absorb_q(to_dev(c.x, dtype), to_dev(qp, dtype) if d_r else None, to_dev(c.w, dtype)))
+    ref = O.absorb_query(G.to_f64(c.x, dtype), G.to_f64(qp, dtype), G.to_f64(c.w, dtype))
+    assert rel_err(got[..., :d_c], ref[..., :d_c]) <= TOL[dtype]
+    assert np.array_equal(got[..., d_c:], ref[..., d_c:])   # q_pe copied bit-exactly
+
+
+# ----------------------------------------------------------------------------
+# the pages' own small workloads end to end
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [G.F32, G.BF16])
+def test_ferrox_shape_chain(dtype):
+    """The ferrox-core unit-test shape: absorb -> latent decode -> up_v equals the
+    unabsorbed attention over per-head expanded K and V."""
+    c = G.p2_tiny_case()
+    st = lambda a: G.storage(a, dtype)
+    scale = 1.0 / math.sqrt(c.d_nope + c.d_r)
+    q = M.absorb_q(to_dev(st(c.q_nope[None]), dtype), to_dev(st(c.q_pe[None]), dtype), to_dev(st(c.w_uk), dtype))
+    lens = torch.tensor([c.seq], dtype=torch.int32).cuda()
+    lat, lse = M.latent_decode(q, to_dev(st(c.latent[None]), dtype), lens, c.d_c, scale)
+    v = to_host64(M.up_v(lat, to_dev(st(c.w_uv), dtype)))[0]
+    f = lambda a: G.to_f64(st(a), dtype)
+    ref, _ = O.mla_unabsorbed(f(c.q_nope), f(c.q_pe), f(c.latent), c.d_c, f(c.w_uk), f(c.w_uv), scale, c.seq)
+    e = rel_err(v, ref)
+    say(f"ferrox chain {dtype}: rel err {e:.2e}")
+    assert e <= TOL[dtype]
+    if dtype == G.F32:
+        assert np.max(np.abs(v - ref)) < 1e-5   # the page's own absolute bound
+
+
+def test_config1_notebook_chain():
+    d = G.config1_notebook(0)
+    scale = 1.0 / math.sqrt(d.d_h)
+    uQ, uK, uV, Ow = O.notebook_split_heads(d.W_uQ, d.W_uK, d.W_uV, d.W_O, d.H)
+    cache = np.vstack([d.C_KV, d.X @ d.W_dKV])                 # host-side append of the new latent
+    q_nope = ((d.X @ d.W_dQ)[0] @ uQ)                           # [H, d_h]
+    st = lambda a: G.storage(a, G.F32)
+    q = M.absorb_q(to_dev(st(q_nope[None]), G.F32), None, to_dev(st(uK.transpose(0, 2, 1)), G.F32))
+    lens = torch.tensor([cache.shape[0]], dtype=torch.int32).cuda()
+    lat, _ = M.latent_decode(q, to_dev(st(cache[None]), G.F32), lens, d.d_c, scale)
+    v = to_host64(M.up_v(lat, to_dev(st(uV.transpose(0, 2, 1)), G.F32)))[0]
+    final = np.einsum("hi,hio->o", v, Ow)
+    v_ref, final_ref = O.notebook_softmax_unabsorbed(d.X, d.W_dQ, d.W_dKV, d.W_uQ, d.W_uK, d.W_uV, d.W_O,
+                                                     d.C_KV, d.H, scale)
+    say(f"config 1: v {rel_err(v, v_ref):.2e} final {rel_err(final, final_ref):.2e}")
+    assert rel_err(v, v_ref) <= 1e-4 and rel_err(final, final_ref) <= 1e-4
+
+
+# ----------------------------------------------------------------------------
+# the log-sum-exp combine on its own
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [G.F32, G.BF16])
+def test_lse_combine(dtype):
+    rng = np.random.default_rng(17)
+    P, R, H, d = 5, 3, 4, 512
+    o = rng.standard_normal((P, R, H, d)).astype(np.float32)
+    l = (rng.standard_normal((P, R, H)) * 20).astype(np.float32)
+    l[1] = -np.inf                      # an empty part everywhere
+    l[:, 2, 3] = -np.inf                # a row/head with nothing at all
+    o[1] = np.nan                       # never read
+    got, glse = M.lse_combine(torch.from_numpy(o).cuda(), torch.from_numpy(l).cuda(), dtype=dtype_torch(dtype))
+    ref, rlse = O.lse_merge(o.astype(np.float64), l.astype(np.float64))
+    assert rel_err(to_host64(got), ref) <= TOL[dtype]
+    assert lse_err(glse.cpu().numpy(), rlse) <= 1e-4
