@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark: DeepSeek-V2-shaped absorbed-MLA decode on one MI355X.
+
+One step = the whole decode path for one batch: the planning kernel, the
+latent attention kernel, the log-sum-exp combine and the W_UV up-projection
+(B=64 sequences x 4096 cached positions, H=128, d_c=512, d_r=64, d_v=128,
+bf16 storage, fp32 accumulation). Inputs are synthetic (seeded), resident in
+HBM before timing, and rotated over several independent copies so the
+256 MiB Infinity Cache cannot serve a step from a previous one.
+
+Prints ONE JSON line. `value` is latent head-tokens attended per second
+(B*H*seq per step). `roofline` is for the dominant kernel (the latent
+attention kernel), timed with HIP events recorded on its own stream.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+workload on this host.
+
+    python bench.py [--steps K] [--warmup W] [--prefill] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+ATTN_SRC = os.path.join(ROOT, "head_latent_attention_09_amd", "csrc", "mla_attn.hip")
+TRAFFIC_FILE = os.path.join(PROFILE_DIR, "latent_attention_decode_b64_h128_s4096_traffic.json")
+
+B, H, S, D_C, D_R, D_V = 64, 128, 4096, 512, 64, 128
+W = D_C + D_R
+ESIZE = 2
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--copies", type=int, default=3, help="rotated input copies")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
+    p.add_argument("--prefill", action="store_true", help="also time the causal-prefill chain (config 5)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    return p.parse_args()
+
+
+def src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(per_launch_alg_bytes):
+    """Measured HBM bytes per attention launch from committed counter runs,
+    valid only for the kernel source they were taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != src_hash(ATTN_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s):
+    """fp64 numpy oracle (latent definition + per-head up-projection) on whole
+    sequences of the same workload until the time budget is spent."""
+    import oracle as O
+    import workloads as G
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cores = min(threads, len(os.sched_getaffinity(0)))
+    wuv = G.to_f64(case.w_uv, G.BF16)
+    done, t0 = 0, time.perf_counter()
+    nseq = 0
+    while True:
+        b = nseq % case.B
+        lat = G.to_f64(case.cache[b], G.BF16)
+        q = G.to_f64(case.q[b], G.BF16)
+        out, _ = O.latent_attention(q, lat, D_C, case.kq_scale, int(case.lens[b]))
+        O.up_project(out[None], wuv)
+        done += H * int(case.lens[b])
+        nseq += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": done / el, "unit": "latent tokens/s (B*H*seq)", "cores": cores, "kind": "oracle",
+            "sample": f"{nseq} whole sequences (H={H}, seq={S}) of the benchmark workload, "
+                      f"fp64 numpy latent definition + up-projection, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(decode would shard by sequence, see DESIGN.md); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import head_latent_attention_09_amd as M
+    import workloads as G
+
+    assert torch.cuda.is_available(), "no HIP device"
+    dev = torch.device("cuda:0")
+    case = G.config3_decode_bf16(0)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q0, cache0, wuv = to_dev(case.q), to_dev(case.cache), to_dev(case.w_uv)
+    lens = torch.from_numpy(case.lens).to(dev)
+    sets = []
+    for i in range(args.copies):
+        q = q0 if i == 0 else q0.clone()
+        cache = cache0 if i == 0 else cache0.clone()
+        sets.append(dict(q=q, cache=cache, out=torch.empty((B, H, D_C), dtype=torch.bfloat16, device=dev),
+                         lse=torch.empty((B, H), dtype=torch.float32, device=dev),
+                         v=torch.empty((B, H, D_V), dtype=torch.bfloat16, device=dev)))
+    G_workers = M.default_workers()
+    ws = torch.empty(M.decode_workspace_bytes(B, H, D_C, G_workers), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        s = sets[i % len(sets)]
+        M.latent_decode(s["q"], s["cache"], lens, D_C, case.kq_scale, out=s["out"], lse=s["lse"],
+                        workspace=ws, timing_events=ev)
+        M.up_v(s["out"], wuv, out=s["v"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    attn_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for a, b_ in attn_ev:  # create the events (lazily created on first record)
+        a.record(stream)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, attn_ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    attn_ms = [a.elapsed_time(b_) for a, b_ in attn_ev]
+    attn_avg = float(np.mean(attn_ms))
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    tokens = B * H * S
+    value = tokens / (ms_step / 1e3)
+    alg_bytes = B * S * W * ESIZE + B * H * W * ESIZE          # latent cache + absorbed queries
+    alg_flop = B * S * H * (2 * W + 2 * D_C)                   # QK (576) + PV (512) per head-position
+    achieved = alg_bytes / (attn_avg / 1e3) / 1e9
+    traffic = traffic_from_profile(alg_bytes)
+    line = {
+        "metric": "latent tokens attended/sec (B*H*seq), H=128 decode",
+        "value": round(value, 1),
+        "unit": "latent tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; RMS-normed latent, roped k_pe/q_pe, q_abs ~ N(0,1/512), W_UV ~ N(0,1/512))",
+        "config": {"workload": "DeepSeek-V2-shaped absorbed decode + W_UV up-projection",
+                   "batch": B, "heads": H, "seq_len": S, "d_c": D_C, "d_r": D_R, "d_v": D_V,
+                   "cache": "dense", "workers": G_workers, "rotated_copies": args.copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "latent attention (mla::mf::attn_mfma_kernel<4>)",
+                     "avg_launch_ms": round(attn_avg, 5), "alg_bytes_per_launch": alg_bytes},
+        "roofline_mfma": {"achieved": round(alg_flop / (attn_avg / 1e3) / 1e12, 1), "peak": BF16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(alg_flop / (attn_avg / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                          "alg_flop_per_launch": alg_flop},
+        "wall_s_timed": round(wall, 3),
+    }
+    if args.prefill:
+        line["prefill"] = bench_prefill(M, G, torch, dev, args)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def bench_prefill(M, G, torch, dev, args):
+    """Causal prefill chain of config 5: absorb -> prefill attention -> up_v."""
+    c = G.config5_prefill_bf16(0)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    Bp, Sp, Hp = c.B, c.S_q, c.H
+    qn = to_dev(c.q_nope).reshape(Bp * Sp, Hp, -1)
+    qp = to_dev(c.q_pe).reshape(Bp * Sp, Hp, -1)
+    wuk, wuv, cache = to_dev(c.w_uk), to_dev(c.w_uv), to_dev(c.cache)
+    q = torch.empty((Bp * Sp, Hp, c.W), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((Bp, Sp, Hp, c.d_c), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Bp, Sp, Hp), dtype=torch.float32, device=dev)
+    v = torch.empty((Bp * Sp, Hp, c.d_v), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(M.prefill_workspace_bytes(Bp, Sp, Hp, c.d_c, 0), dtype=torch.uint8, device=dev)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
+    def step(e=None):
+        M.absorb_q(qn, qp, wuk, out=q)
+        M.latent_prefill_causal(q.view(Bp, Sp, Hp, -1), cache, c.d_c, c.kq_scale, out=out, lse=lse,
+                                workspace=ws, timing_events=e)
+        M.up_v(out.view(Bp * Sp, Hp, -1), wuv, out=v)
+
+    steps = max(3, args.steps // 10)
+    for _ in range(2):
+        step(ev)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    attn = []
+    t0.record()
+    for _ in range(steps):
+        e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        e[0].record(); e[1].record()
+        step(e)
+        attn.append(e)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in attn]))
+    pairs = Bp * Hp * Sp * (Sp + 1) // 2
+    flop = pairs * (2 * c.W + 2 * c.d_c)
+    return {"workload": "causal prefill B=2 S=4096 H=128 (absorb + attention + up_v)",
+            "ms_per_step": round(ms, 4), "latent_tokens_per_s": round(pairs / (ms / 1e3), 1),
+            "attention_ms": round(attn_ms, 4),
+            "attention_mfma_tflops": round(flop / (attn_ms / 1e3) / 1e12, 1),
+            "attention_mfma_frac": round(flop / (attn_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
+if __name__ == "__main__":
+    main()

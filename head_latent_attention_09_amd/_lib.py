@@ -94,6 +94,9 @@ def _stream():
 def _events(timing_events):
     if timing_events is None:
         return None
+    for e in timing_events:  # torch creates the underlying hipEvent_t on first record
+        if not e.cuda_event:
+            e.record(torch.cuda.current_stream())
     arr = (ctypes.c_void_p * 2)(timing_events[0].cuda_event, timing_events[1].cuda_event)
     return ctypes.cast(arr, ctypes.c_void_p), arr  # keep arr alive with the pointer
 

@@ -52,7 +52,8 @@ template <> __device__ __forceinline__ void store_f32<bf16>(bf16* p, float v) { 
 struct Plan {
   int32_t* cum;     // [R + 1]: exclusive prefix sum of tiles per row (cum[R] = total)
   int32_t* len;     // [R]: visible positions per row (clamped)
-  int32_t* flags;   // [R]: set when a row must be recomputed by the generic kernel
+  int32_t* flags;   // [R]: set when a row had to be recomputed (see the attention kernel)
+  int32_t* split;   // [1 + G]: count, then the rows cut by a worker boundary
   float* part_o;    // [2G, H, d_c]
   float* part_lse;  // [2G, H]
   int R;
@@ -62,10 +63,11 @@ struct Plan {
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// workspace layout: cum | len | flags | part_o | part_lse
+// workspace layout: cum | len | flags | split | part_o | part_lse
 inline size_t plan_bytes(int64_t R, int G, int H, int d_c) {
   size_t b = align256(sizeof(int32_t) * (size_t)(R + 1));
   b += 2 * align256(sizeof(int32_t) * (size_t)R);
+  b += align256(sizeof(int32_t) * (size_t)(G + 1));
   b += align256(sizeof(float) * (size_t)2 * G * H * d_c);
   b += align256(sizeof(float) * (size_t)2 * G * H);
   return b;
@@ -80,6 +82,8 @@ inline Plan plan_layout(void* ws, int R, int G, int H, int d_c, int tile) {
   p += align256(sizeof(int32_t) * (size_t)R);
   pl.flags = (int32_t*)p;
   p += align256(sizeof(int32_t) * (size_t)R);
+  pl.split = (int32_t*)p;
+  p += align256(sizeof(int32_t) * (size_t)(G + 1));
   pl.part_o = (float*)p;
   p += align256(sizeof(float) * (size_t)2 * G * H * d_c);
   pl.part_lse = (float*)p;
