@@ -272,8 +272,11 @@ constexpr int TILE = 32;                   // positions per tile
 constexpr int C_BYTES = TILE * DC * 2;     // latent part of a tile: 32 rows x 1024 B
 constexpr int TILE_BYTES = TILE * WD * 2;  // + rope part: 32 rows x 128 B = 36 KiB
 constexpr int NSTAGE = 3;                  // tiles in the LDS ring
-constexpr int KQR = 28;                    // query k-steps held in registers (dims 0..447)
-constexpr int QL_BYTES = 128 * 128 * 2;   // dims 448..575 of the 128 query rows, kept in LDS
+constexpr int KQR = 24;                    // query k-steps held in registers (dims 0..383)
+constexpr int QLW = WD - 16 * KQR;         // query dims kept in LDS (384..575)
+constexpr int QL_ROW = QLW * 2;            // bytes per head row of that block (24 chunks)
+constexpr int QL_BYTES = 128 * QL_ROW;     // 48 KiB for the 128 query rows
+constexpr int RING = 4;                    // LDS operand reads in flight per wave
 constexpr int NW = 4;                      // waves per workgroup (32 heads each)
 constexpr int LPW = 36 / NW;               // tile loads per wave
 constexpr float SLACK = 64.0f;             // log2 units a score may exceed the reference max
@@ -430,19 +433,20 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
   // B operand of S^T = K Q^T (lane: head h, dims 16ks + 8g .. +7)
   for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < ntiles) issue_tile(a, smem + s * TILE_BYTES, b, (lt0 + s) * TILE, len, lane, wv);
-  // this wave's 32 query rows: dims 0..447 (28 k-steps) in registers as the
+  // this wave's 32 query rows: dims 0..383 (24 k-steps) in registers as the
   // B operand of S^T = K Q^T (lane: head h, dims 16ks + 8g .. +7); dims
-  // 448..575 go to LDS, head row hr at ql + hr*256, chunk c at c ^ (hr & 15),
-  // one 8 KiB block per wave.
+  // 384..575 go to LDS, head row hr at ql + hr*QL_ROW, chunk c (of 24) at
+  // c ^ sR(hr), one 12 KiB block per wave.
   const int hq = h < H ? h : H - 1;  // waves past the last head compute on a copy and write nothing
-  char* ql = smem + NSTAGE * TILE_BYTES + wv * 8192;
+  char* ql = smem + NSTAGE * TILE_BYTES + wv * (32 * QL_ROW);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < 32 * QL_ROW / 1024; ++k) {
     const int p = k * 64 + lane;     // 16-byte chunk position in this wave's block
-    const int hr = p >> 4;
+    const int hr = p / (QL_ROW / 16);
+    const int pc = p - hr * (QL_ROW / 16);
     const int hsrc = wv * 32 + hr < H ? wv * 32 + hr : H - 1;
     const char* qbase = (const char*)(a.q + (size_t)r * H * WD + 16 * KQR);
-    dma16(qbase, (uint32_t)(hsrc * (WD * 2) + (((p & 15) ^ (hr & 15)) << 4)), lds_addr(ql + k * 1024));
+    dma16(qbase, (uint32_t)(hsrc * (WD * 2) + ((pc ^ sR(hr)) << 4)), lds_addr(ql + k * 1024));
   }
   bf16x8 qf[KQR];
   {
@@ -488,8 +492,8 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
     const int gg = ln >> 5;
     const int baseC = mrow * 1024 + ((gg ^ (sCm & 1)) << 4);
     const int baseR = C_BYTES + mrow * 128 + ((gg ^ (sRm & 1)) << 4);
-    const int baseQ = mrow * 256 + ((gg ^ (mrow & 1)) << 4);
-    const int xC = sCm >> 1, xR = sRm >> 1, xQ = (mrow & 15) >> 1;
+    const int baseQ = mrow * QL_ROW + ((gg ^ (sRm & 1)) << 4);
+    const int xC = sCm >> 1, xR = sRm >> 1;
     const int q16 = ln & 15;
     const int rowA = 4 * gg + (q16 >> 2);  // PV: rows of the first transposing load (k-step 0)
     const int rowB = rowA + 8;
@@ -499,42 +503,39 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
     const int baseB = rowB * 1024 + ((cb ^ (sB & 3)) << 4) + (q16 & 1) * 8;
     const int xA = sA >> 2, xB = sB >> 2;
 
-    // ---- S^T[position][head] = K_tile . Q^T, 36 k-steps of 16 dims. Operand
-    // reads run one k-step pair ahead of the MFMAs; the compiler barriers
-    // keep the scheduler from hoisting every read (and its registers) up front.
+    // ---- S^T[position][head] = K_tile . Q^T, 36 k-steps of 16 dims. LDS
+    // operands are read RING k-steps ahead of their MFMA; the compiler
+    // barriers keep reads in this order (neither hoisted nor sunk).
     f32x16 sacc;
     {
-      // A operand (K tile rows) of k-step ks; B operand from registers (ks < 32) or LDS
+      // A operand (K tile rows) of k-step ks
       auto kread = [&](int ks) -> bf16x8 {
-        const char* p = ks < 32 ? buf + baseC + ((((ks & 7) ^ xC)) << 5) + 256 * (ks >> 3)
+        const char* p = ks < 32 ? buf + baseC + (((ks & 7) ^ xC) << 5) + 256 * (ks >> 3)
                                 : buf + baseR + (((ks - 32) ^ xR) << 5);
         return *(const MLA_LDS bf16x8*)p;
       };
+      // B operand of k-steps ks >= KQR (query dims kept in LDS)
       auto qread = [&](int ks) -> bf16x8 {
-        return *(const MLA_LDS bf16x8*)(ql + baseQ + (((ks - KQR) ^ xQ) << 5));
+        const int kq = ks - KQR;
+        return *(const MLA_LDS bf16x8*)(ql + baseQ + 128 * (kq >> 2) + (((kq & 3) ^ xR) << 5));
       };
-      bf16x8 k0 = kread(0), k1 = kread(1);
+      bf16x8 kr[RING], qr[RING];
 #pragma unroll
-      for (int ks = 0; ks < 36; ks += 2) {
-        bf16x8 n0 = k0, n1 = k1;
-        if (ks + 2 < 36) {
-          n0 = kread(ks + 2);
-          n1 = kread(ks + 3);
-        }
-        bf16x8 b0, b1;
-        if (ks < KQR) {
-          b0 = qf[ks];
-          b1 = qf[ks + 1];
-        } else {
-          b0 = qread(ks);
-          b1 = qread(ks + 1);
+      for (int i = 0; i < RING; ++i) {
+        kr[i] = kread(i);
+        if (i >= KQR) qr[i] = qread(i);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 36; ++ks) {
+        const bf16x8 a_op = kr[ks % RING];
+        const bf16x8 b_op = ks < KQR ? qf[ks] : qr[ks % RING];
+        if (ks + RING < 36) {
+          kr[ks % RING] = kread(ks + RING);
+          if (ks + RING >= KQR) qr[ks % RING] = qread(ks + RING);
         }
         asm volatile("" ::: "memory");
-        if (ks == 0) mfma_vacc_first(sacc, k0, b0);
-        else mfma_vacc(sacc, k0, b0);
-        mfma_vacc(sacc, k1, b1);
-        k0 = n0;
-        k1 = n1;
+        if (ks == 0) mfma_vacc_first(sacc, a_op, b_op);
+        else mfma_vacc(sacc, a_op, b_op);
       }
     }
     // the last QK MFMA's result is read by VALU next: 8-pass XDL -> VALU read
@@ -550,7 +551,7 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
       tmax = fmaxf(tmax, i < nvalid ? sacc[rr] * a.scale_log2 : -INFINITY);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (m_ref == -INFINITY) m_ref = tmax;  // first tile of the segment
+    m_ref = m_ref == -INFINITY ? tmax : m_ref;  // first tile of the segment
     overflow |= tmax > m_ref + SLACK;
     bf16x8 pb[2];
     float psum = 0.f;
@@ -569,27 +570,28 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
     // the S accumulators): lane group (l/16) reads positions 16kk + 4g + {0..3}
     // and the same +8, 16 dims each.
     typedef short s16x8 __attribute__((ext_vector_type(8)));
+    // 32 PV steps j = 16 kk + db; transposing reads run RING steps ahead
+    auto vread = [&](int j, bool second) -> s16x4 {
+      const int kk = j >> 4, db = j & 15;
+      const char* p = buf + (second ? baseB + (((db & 3) ^ xB) << 6) : baseA + (((db & 3) ^ xA) << 6)) +
+                      256 * (db >> 2) + kk * 16 * 1024;
+      return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)p);
+    };
+    s16x4 va[RING], vb[RING];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      auto vread = [&](int db, bool second) -> s16x4 {
-        const char* p = buf + (second ? baseB + (((db & 3) ^ xB) << 6) : baseA + (((db & 3) ^ xA) << 6)) +
-                        256 * (db >> 2) + kk * 16 * 1024;
-        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)p);
-      };
-      s16x4 va = vread(0, false), vb = vread(0, true);
+    for (int i = 0; i < RING; ++i) {
+      va[i] = vread(i, false);
+      vb[i] = vread(i, true);
+    }
 #pragma unroll
-      for (int db = 0; db < 16; ++db) {
-        s16x4 na = va, nb = vb;
-        if (db + 1 < 16) {
-          na = vread(db + 1, false);
-          nb = vread(db + 1, true);
-        }
-        asm volatile("" ::: "memory");
-        s16x8 v8 = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pb[kk], o[db], 0, 0, 0);
-        va = na;
-        vb = nb;
+    for (int j = 0; j < 32; ++j) {
+      const s16x8 v8 = __builtin_shufflevector(va[j % RING], vb[j % RING], 0, 1, 2, 3, 4, 5, 6, 7);
+      if (j + RING < 32) {
+        va[j % RING] = vread(j + RING, false);
+        vb[j % RING] = vread(j + RING, true);
       }
+      asm volatile("" ::: "memory");
+      o[j & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pb[j >> 4], o[j & 15], 0, 0, 0);
     }
   }
   // Overflow of the fixed reference (see above): the first workgroup to flag
