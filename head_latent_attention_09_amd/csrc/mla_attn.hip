@@ -63,6 +63,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(RowMap m, Plan pl, int H, in
     const int n = (pl.len[r] + tile - 1) / tile;
     pl.cum[r] = base;
     if (n > 0 && base / per != (base + n - 1) / per) pl.split[1 + atomicAdd(&nsplit, 1)] = r;
+    // workers whose range starts inside this row's tiles begin with this row
+    for (int w = (base + per - 1) / per; n > 0 && w * per < base + n && w < pl.G; ++w) pl.wrow[w] = r;
     base += n;
   }
   if (tid == 1023) pl.cum[R] = total;
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(NT) void attn_generic_kernel(Args<T> a) {
   const int t_begin = w * per;
   if (t_begin >= total) return;
   const int t_end = min(t_begin + per, total);
-  for (int r = plan_row_of(a.pl.cum, a.pl.R, t_begin); r < a.pl.R; ++r) {
+  for (int r = a.pl.wrow[w]; r < a.pl.R; ++r) {
     const int c0 = a.pl.cum[r], c1 = a.pl.cum[r + 1];
     if (c0 >= t_end) break;
     if (c1 <= t_begin || c1 == c0) continue;
@@ -264,30 +266,58 @@ __global__ __launch_bounds__(NT) void attn_generic_kernel(Args<T> a) {
 }  // namespace gn
 
 // ===========================================================================
-// bf16 MFMA attention: d_c = 512, d_r = 64, 4 waves x 32 heads
+// bf16 MFMA attention: d_c = 512, d_r = 64, 32..128 heads
 // ===========================================================================
 namespace mf {
 constexpr int DC = 512, DR = 64, WD = 576;
-constexpr int TILE = 32;                   // positions per tile
-constexpr int C_BYTES = TILE * DC * 2;     // latent part of a tile: 32 rows x 1024 B
-constexpr int TILE_BYTES = TILE * WD * 2;  // + rope part: 32 rows x 128 B = 36 KiB
-constexpr int NSTAGE = 3;                  // tiles in the LDS ring
-constexpr int KQR = 24;                    // query k-steps held in registers (dims 0..383)
-constexpr int QLW = WD - 16 * KQR;         // query dims kept in LDS (384..575)
-constexpr int QL_ROW = QLW * 2;            // bytes per head row of that block (24 chunks)
-constexpr int QL_BYTES = 128 * QL_ROW;     // 48 KiB for the 128 query rows
-constexpr int RING = 4;                    // LDS operand reads in flight per wave
-constexpr int NW = 4;                      // waves per workgroup (32 heads each)
-constexpr int LPW = 36 / NW;               // tile loads per wave
-constexpr float SLACK = 64.0f;             // log2 units a score may exceed the reference max
+constexpr int TILE = 16;                     // positions per tile
+constexpr int C_BYTES = TILE * DC * 2;       // latent rows: 16 x 1024 B
+constexpr int TILE_BYTES = TILE * WD * 2;    // + rope rows: 16 x 128 B = 18 KiB
+constexpr int NBUF = 4;                      // tile buffers in LDS
+constexpr int AHEAD = NBUF - 1;              // tiles issued ahead of the tile whose values are read
+constexpr int KS = WD / 32;                  // k-steps of 32 dims in the score contraction (18)
+constexpr int KL = DC / 32;                  // k-steps over the latent dims (16); the rest are rope dims
+constexpr int KQ = 12;                       // k-steps whose query operand stays in registers
+constexpr int NW = 4;                        // waves per workgroup
+constexpr int QR_ROW = (WD - 32 * KQ) * 2 + 16;     // query rest: bytes per head row (16 B of padding)
+constexpr int QR_BYTES = 13 * 1024;                 // per wave: 32 rows of QR_ROW bytes, in whole 1 KiB loads
+constexpr int P_BYTES = 32 * NW * TILE * 2;  // bf16 softmax weights of one tile, 128 heads (4 KiB)
+constexpr int RING = 6;                      // score operand (tile) reads in flight per wave
+constexpr int QA = 2;                        // k-steps the query operand reads from LDS run ahead
+constexpr int DW = DC / NW;                  // output dims per wave in the value product
+constexpr float SLACK = 64.0f;               // log2 units a score may exceed the reference max
+constexpr int LDS_QR = NBUF * TILE_BYTES;
+constexpr int LDS_P = LDS_QR + NW * QR_BYTES;
+constexpr int LDS_INV = LDS_P + 2 * P_BYTES;
+constexpr int SMEM_BYTES = LDS_INV + 32 * NW * 4;
 
-// LDS tile layout. Latent region: row r at r*1024, its 16-byte chunk c at
-// position c ^ sC(r) (XOR inside aligned groups of 16 chunks). Rope region:
-// row r at C_BYTES + r*128, chunk c at c ^ sR(r). The XOR patterns make the
-// two read patterns conflict-free for a 128- or 256-byte-wide LDS:
-//  (a) QK operand: 32 rows, one chunk each (sC, sR distinct over 8/16 rows);
-//  (b) PV operand, transposing loads: 4 consecutive rows x 4 chunks
-//      (sC's bits 1-3 spread the 4 rows over distinct chunk pairs/quads).
+// Work split inside a workgroup (4 waves, one per SIMD). Scores and softmax
+// weights are split by head: wave w owns heads 32w .. 32w+31 and computes
+// S^T = K_tile Q^T for them (18 k-steps x 2 head blocks of 16x16x32). The
+// bf16 weights go through LDS and the value product is split by output dims:
+// wave w accumulates O^T[128w .. 128w+127][all heads] (4 x 4 MFMAs of
+// 32x32x16), so each wave reads a quarter of the tile's values.
+//
+// Software pipeline, one workgroup barrier per tile. Iteration i:
+//   scores of tile i+1, with the softmax of tile i (scores from the previous
+//   iteration) and the loads of tile i+AHEAD placed between the MFMAs;
+//   value fragments of tile i; weights of tile i to LDS; barrier; weight
+//   fragments of tile i and the first score operands of tile i+2; value
+//   product of tile i.
+// Tile j is loaded into buffer j % NBUF during iteration j - AHEAD, after the
+// barrier that ends every read of the buffer's previous tile j - NBUF (its
+// value fragments are read, and waited for, before the barrier of iteration
+// j - NBUF), and published by the barrier of iteration j - 2.
+//
+// LDS layouts (XOR swizzles keep every read and write pattern below free of
+// bank conflicts on a 256-byte-wide LDS):
+//   tile latent row t at t*1024, 16-byte chunk c at c ^ sC(t) inside its
+//     aligned group of 16 chunks; rope row t at C_BYTES + t*128, chunk c at
+//     c ^ sR(t);
+//   query dims 32KQ .. 575: wave block of 32 rows of QR_ROW bytes (the 16
+//     bytes of padding shift consecutive rows across the banks);
+//   weights: head hh at hh*32 (16 positions), 8-byte quarter q at
+//     q ^ (2 * ((hh >> 3) & 1)).
 __device__ __forceinline__ int sC(int r) {
   return (((r & 1) ? 6 : 0) ^ ((r & 2) ? 10 : 0)) ^ ((r >> 2) & 3);
 }
@@ -304,16 +334,18 @@ struct Args {
   float* lse;
 };
 
-// S^T accumulation with the accumulator pinned to VGPRs: the 256 AGPRs hold
-// the output accumulator, and the compiler otherwise puts S there too and
-// evicts the query fragments to scratch. Consecutive MFMAs accumulating into
-// the same registers need no wait states between them.
-__device__ __forceinline__ void mfma_vacc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Score MFMAs with the accumulator pinned to VGPRs (the AGPRs hold the output
+// accumulator). Invisible to the compiler's hazard checker: a VALU read of
+// the result must be at least 11 wait states after the MFMA (see sync_scores).
+__device__ __forceinline__ void mfma16(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma_vacc_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+__device__ __forceinline__ void mfma16_first(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
+__device__ __forceinline__ void sync_scores() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
 
 // Direct global->LDS load of 64 lanes x 16 bytes: lane l reads 16 bytes at
 // gbase + voff and writes them to LDS address lds + 16 l. Issued from inline
@@ -325,6 +357,13 @@ __device__ __forceinline__ void mfma_vacc_first(f32x16& acc, const bf16x8& a, co
 // the load that reads it. The kernel makes no other use of M0.
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(gbase), "s"(lds) : "memory");
+}
+// The same for data read once (cache tiles): non-temporal, so the stream does
+// not displace reused lines; measured 1.27x the streaming rate of the
+// default policy for this load pattern.
+__device__ __forceinline__ void dma16_stream(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :: "v"(voff), "s"(gbase), "s"(lds) : "memory");
 }
 
@@ -342,10 +381,33 @@ __device__ __forceinline__ void opaque(T& x) {
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0, "");
-  constexpr int n = N > 63 ? 63 : N;
+  static_assert(N >= 0 && N <= 63, "");
   // vmcnt in bits [3:0] and [15:14]; expcnt (7) and lgkmcnt (15) left unconstrained
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// vmcnt wait with a run-time count: a jump table of immediate waits (counts
+// above 63 wait for 63, which waits for more than asked)
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define MLA_W(k) \
+  case k:        \
+    wait_vmcnt<k>(); \
+    break;
+#define MLA_W8(k) MLA_W(k) MLA_W(k + 1) MLA_W(k + 2) MLA_W(k + 3) MLA_W(k + 4) MLA_W(k + 5) MLA_W(k + 6) MLA_W(k + 7)
+    MLA_W8(0) MLA_W8(8) MLA_W8(16) MLA_W8(24) MLA_W8(32) MLA_W8(40) MLA_W8(48) MLA_W8(56)
+#undef MLA_W8
+#undef MLA_W
+    default:
+      wait_vmcnt<63>();
+  }
+}
+
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
+
+// v from lane (ln ^ mask); ln is the caller's (opaque) lane id
+__device__ __forceinline__ float shfl_xor(float v, int ln, int mask) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((ln ^ mask) << 2, __builtin_bit_cast(int, v)));
 }
 
 __device__ __forceinline__ void block_barrier() {
@@ -354,39 +416,52 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Issue the direct global->LDS loads of one tile (positions t0 .. t0+31 of
-// batch entry b). 36 loads of 64 lanes x 16 B: load ld < 32 fills latent row
-// ld (1 KiB, one row); load 32 + j fills the rope chunks of rows 8j .. 8j+7.
-// Wave wv issues loads wv, wv + NW, ... Rows at or past `len` re-read row
-// len-1 (finite data; their scores are masked to -inf).
-__device__ __forceinline__ void issue_tile(const Args& a, char* buf, int b, int t0, int len, int lane, int wv) {
+// Source of one tile: row 0 of positions t0 .. t0+15 of batch entry b in
+// global memory, and the last row of it that is visible.
+struct TileSrc {
+  const char* p;
+  int last;
+};
+
+__device__ __forceinline__ TileSrc tile_src(const Args& a, int b, int t0, int len) {
   const RowMap& m = a.map;
-  const char* tile;
+  TileSrc s;
   if (m.mode == 1) {
     const int pg = page_of(m, b, t0);
-    tile = (const char*)(a.cache + ((size_t)pg * m.page_size + (t0 % m.page_size)) * WD);
+    s.p = (const char*)(a.cache + ((size_t)pg * m.page_size + (t0 % m.page_size)) * WD);
   } else {
-    tile = (const char*)(a.cache + dense_row(m, b, t0, WD));
+    s.p = (const char*)(a.cache + dense_row(m, b, t0, WD));
   }
-  const int last = len - 1 - t0;  // last valid row of this tile (wave-uniform)
-  // Latent rows ld = wv + 4k (k < 8): sC(ld) = f(wv) ^ (k & 3), so the lane's
-  // chunk is (lane ^ f(wv)) ^ (k & 3); the row pointer is wave-uniform.
-  int lx = lane ^ sC(wv);
-  opaque(lx);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  s.last = len - 1 - t0;
+  return s;
+}
+
+// Loads of one tile: 18 loads of 64 lanes x 16 B. Load k < 4 of wave wv fills
+// latent row wv + 4k (1 KiB); load 4 of waves 0 and 1 the rope chunks of
+// rows 8wv .. 8wv+7 (one load issue costs the issuing wave about as much as
+// another, so the two rope loads are not split four ways). Rows past the last
+// visible one re-read it (finite data; their weights are zeroed). lx is
+// lane ^ sC(wv): sC(wv + 4k) = sC(wv) ^ k.
+__device__ __forceinline__ int loads_per_tile(int wv) { return wv < 2 ? 5 : 4; }
+
+__device__ __forceinline__ void issue_load(const TileSrc& s, char* buf, int k, int lx, int lane, int wv) {
+  if (k < 4) {
     const int ld = wv + NW * k;
-    const int row = ld < last ? ld : last;
-    dma16(tile + (size_t)row * (WD * 2), (uint32_t)((lx ^ (k & 3)) << 4), lds_addr(buf + ld * 1024));
-  }
-  // rope chunks of rows 8wv .. 8wv+7: lane -> row 8wv + lane/8, chunk (lane%8) ^ sR(row)
-  {
-    const int rl = NW * 2 * wv + (lane >> 3);
-    const int row = rl < last ? rl : last;
-    dma16(tile, (uint32_t)(row * (WD * 2) + DC * 2 + (((lane & 7) ^ sR(rl)) << 4)),
-          lds_addr(buf + C_BYTES + wv * 1024));
+    const int row = ld < s.last ? ld : s.last;
+    dma16_stream(s.p + (size_t)row * (WD * 2), (uint32_t)((lx ^ k) << 4), lds_addr(buf + ld * 1024));
+  } else if (wv < 2) {
+    const int rl = 8 * wv + (lane >> 3);
+    const int row = rl < s.last ? rl : s.last;
+    dma16_stream(s.p, (uint32_t)(row * (WD * 2) + DC * 2 + (((lane & 7) ^ sR(rl)) << 4)),
+                 lds_addr(buf + C_BYTES + wv * 1024));
   }
 }
+
+__device__ __forceinline__ void issue_tile(const TileSrc& s, char* buf, int lx, int lane, int wv) {
+#pragma unroll
+  for (int k = 0; k < 5; ++k) issue_load(s, buf, k, lx, lane, wv);
+}
+
 
 // Whole-row recompute with the generic kernel (running max with rescaling),
 // writing the final result; the tile ring is reused as its scratch.
@@ -415,190 +490,317 @@ __device__ void recompute_row(const Args& a, int r, char* smem) {
   __syncthreads();
 }
 
+template <int NHB>
 __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, int lt1, bool full, int slot,
                                                char* smem, int* seg_flag, int lane, int wv) {
-  const int H = a.H;
+  constexpr int H = 32 * NHB;
   const int len = a.pl.len[r];
   const int b = row_batch(a.map, r);
-  const int g = lane >> 5;              // half of the wave
-  const int h = wv * 32 + (lane & 31);  // this lane's head (MFMA column)
-  const bool active = wv * 32 < H;      // waves past the last head only help load tiles
+  const bool owner = wv < NHB;  // the wave scores heads 32wv .. 32wv+31
+  // Waves without heads (fewer than 128) also load a query block and score
+  // the first tile (results unused): every path into the tile loop then passes
+  // the compiler's waits for the query registers.
+  const int wq = owner ? wv : 0;
   const int ntiles = lt1 - lt0;
+  const int L = loads_per_tile(wv);
+  char* const qr_lds = smem + LDS_QR + wv * QR_BYTES;
+  float* const inv_s = (float*)(smem + LDS_INV);
+  auto tbuf = [&](int j) { return smem + (j % NBUF) * TILE_BYTES; };
 
-  // every wave must be done with the previous segment's LDS tiles (and flag)
+  // every wave must be done with the previous segment's LDS (and flag)
   block_barrier();
   if (threadIdx.x == 0) *seg_flag = 0;
 
-  // prologue: first NSTAGE-1 tiles, then this wave's 32 query rows as the
-  // B operand of S^T = K Q^T (lane: head h, dims 16ks + 8g .. +7)
-  for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < ntiles) issue_tile(a, smem + s * TILE_BYTES, b, (lt0 + s) * TILE, len, lane, wv);
-  // this wave's 32 query rows: dims 0..383 (24 k-steps) in registers as the
-  // B operand of S^T = K Q^T (lane: head h, dims 16ks + 8g .. +7); dims
-  // 384..575 go to LDS, head row hr at ql + hr*QL_ROW, chunk c (of 24) at
-  // c ^ sR(hr), one 12 KiB block per wave.
-  const int hq = h < H ? h : H - 1;  // waves past the last head compute on a copy and write nothing
-  char* ql = smem + NSTAGE * TILE_BYTES + wv * (32 * QL_ROW);
-#pragma unroll
-  for (int k = 0; k < 32 * QL_ROW / 1024; ++k) {
-    const int p = k * 64 + lane;     // 16-byte chunk position in this wave's block
-    const int hr = p / (QL_ROW / 16);
-    const int pc = p - hr * (QL_ROW / 16);
-    const int hsrc = wv * 32 + hr < H ? wv * 32 + hr : H - 1;
-    const char* qbase = (const char*)(a.q + (size_t)r * H * WD + 16 * KQR);
-    dma16(qbase, (uint32_t)(hsrc * (WD * 2) + ((pc ^ sR(hr)) << 4)), lds_addr(ql + k * 1024));
-  }
-  bf16x8 qf[KQR];
+  // ---- prologue: tiles 0 and 1, the query's rope dims to LDS, tiles 2 ..
+  // AHEAD-1, the query's latent dims to registers (B operand of 16x16x32:
+  // lane l holds head 16hb + l%16 of the wave's 32, dims 32ks + 8(l/16) .. +7)
+  bf16x8 qf[2][KQ];
   {
-    const bf16* qrow = a.q + ((size_t)r * H + hq) * WD + g * 8;
+    int ln = lane;  // per-lane offsets stay in this segment's code (see the tile loop)
+    opaque(ln);
+    const int lx = ln ^ sC(wv);
+    const int np = ntiles < AHEAD ? ntiles : AHEAD;
+    for (int j = 0; j < (np < 2 ? np : 2); ++j) issue_tile(tile_src(a, b, (lt0 + j) * TILE, len), tbuf(j), lx, ln, wv);
+    {
+      const char* qbase = (const char*)(a.q + ((size_t)r * H + wq * 32) * WD + 32 * KQ);
+      constexpr int QC = QR_ROW / 16;  // 16-byte slots per row, the last one padding
 #pragma unroll
-    for (int ks = 0; ks < KQR; ++ks) qf[ks] = *(const bf16x8*)(qrow + ks * 16);
+      for (int k = 0; k < QR_BYTES / 1024; ++k) {
+        const int p = k * 64 + ln;  // 16-byte slot of this wave's block
+        int hr = p / QC, pc = p - hr * QC;
+        if (hr > 31 || pc == QC - 1) hr = pc = 0;  // padding and slack: any valid chunk
+        dma16(qbase, (uint32_t)(hr * (WD * 2) + (pc << 4)), lds_addr(qr_lds + k * 1024));
+      }
+    }
+    for (int j = 2; j < np; ++j) issue_tile(tile_src(a, b, (lt0 + j) * TILE, len), tbuf(j), lx, ln, wv);
+    {
+      const bf16* qrow = a.q + ((size_t)r * H + wq * 32 + (ln & 15)) * WD + (ln >> 4) * 8;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int ks = 0; ks < KQ; ++ks) qf[hb][ks] = *(const bf16x8*)(qrow + hb * 16 * WD + ks * 32);
+    }
+    // tiles 0, 1 and the query rope dims complete; the later tiles and the
+    // query registers (waited for by the compiler) may be in flight
+    wait_vm((np > 2 ? np - 2 : 0) * L + 2 * KQ);
   }
-  wait_vmcnt<0>();  // query rows (and the prologue) complete before the loop
+  block_barrier();
+
+  // ---- per-lane LDS offsets, computed once per segment from an opaque lane
+  // id (values derived from the plain lane id get hoisted out of the segment
+  // loop and spilled); per tile only the buffer base is added
+  int ln = lane;
+  opaque(ln);
+  const int t16 = ln & 15, q4 = ln >> 4;
+  // score A operand (tile rows, lane: row l%16, dims 8(l/16) .. +7 of the
+  // k-step): latent k-step ks: chunk 4ks + l/16 at (4(ks&3) + l/16) ^ sC(row)
+  // in group ks/4, i.e. kofs[ks&3] + 256(ks/4); rope k-steps at rofs[]
+  int kofs[4], rofs[2];
+  {
+    const int y = q4 ^ sC(t16);
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) kofs[a4] = t16 * 1024 + 16 * (y & 3) + 64 * (a4 ^ (y >> 2));
+    const int pr = q4 ^ sR(t16);
+    rofs[0] = C_BYTES + t16 * 128 + 16 * pr;
+    rofs[1] = C_BYTES + t16 * 128 + 16 * (pr ^ 4);
+  }
+  // score B operand of k-steps KQ + k (query dims in LDS): chunk 4k + l/16 of
+  // row 16hb + l%16
+  const int qofs = LDS_QR + wv * QR_BYTES + t16 * QR_ROW + 16 * q4;
+  // value A operand (transposing loads, lane l: dim 128wv + 32d + l%32,
+  // positions 8(l/32) .. +3 from vofs[d], +4 .. +7 from vofs[4 + d])
+  // (rows tA and tA + 4 have the same sC bits 2-3: vx = 64 (sC >> 2) serves both)
+  int vA, vB, vx;
+  {
+    const int tA = 8 * (q4 >> 1) + (t16 >> 2), tB = tA + 4;
+    const int cb = 2 * (q4 & 1) + ((t16 & 3) >> 1);
+    const int sA = sC(tA), sB = sC(tB);
+    vA = tA * 1024 + ((cb ^ (sA & 3)) << 4) + (t16 & 1) * 8 + 256 * wv;
+    vB = tB * 1024 + ((cb ^ (sB & 3)) << 4) + (t16 & 1) * 8 + 256 * wv;
+    vx = (sA >> 2) << 6;
+  }
+  // weights: this lane's 4 positions of head 32wv + 16hb + l%16 (write), and
+  // positions 8(l/32) .. +7 of head 32hb + l%32 (read)
+  const int pwo = LDS_P + (wv * 32 + t16) * 32 + ((q4 ^ (2 * ((ln >> 3) & 1))) << 3);
+  const int pro = LDS_P + (ln & 31) * 32 + (((ln >> 5) ^ ((ln >> 3) & 1)) << 4);
+  // tile loads: latent load k reads chunk (lane ^ sC(wv) ^ k); the rope load
+  // (waves 0, 1) reads row 8wv + l/8, chunk (l&7) ^ sR(row)
+  const int dofs = (ln ^ sC(wv)) << 4;
+  const int rrow = 8 * wv + (ln >> 3);
+  const int rdofs = DC * 2 + (((ln & 7) ^ sR(rrow)) << 4);
+
+  auto load_tile = [&](const TileSrc& s, int boff, int k) {
+    char* buf = smem + boff;
+    if (k < 4) {
+      const int ld = wv + NW * k;
+      const int row = ld < s.last ? ld : s.last;
+      dma16_stream(s.p + (size_t)row * (WD * 2), (uint32_t)(dofs ^ (k << 4)), lds_addr(buf + ld * 1024));
+    } else if (wv < 2) {
+      const int row = s.last >= TILE - 1 ? rrow : (rrow < s.last ? rrow : s.last);
+      dma16_stream(s.p, (uint32_t)(row * (WD * 2) + rdofs), lds_addr(buf + C_BYTES + wv * 1024));
+    }
+  };
+
+  float m_ref[2] = {0.f, 0.f};  // per owned head: reference max (log2 units)
+  float lsum[2] = {0.f, 0.f};   // per owned head: this lane's part of the denominator
+  float ovm = -INFINITY;        // largest score minus reference seen by this lane
+  f32x4 s0[2], s1[2];           // scores of two consecutive tiles (S^T blocks per 16 heads)
+  bf16x8 kr[RING];              // score operand ring
+  f32x16 o[NHB][4];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[hb][d] = f32x16{};
+
+  auto kread = [&](int boff, int ks) -> bf16x8 {
+    const int off = ks < KL ? kofs[ks & 3] + 256 * (ks >> 2) : rofs[ks - KL];
+    return *(const MLA_LDS bf16x8*)(smem + boff + off);
+  };
+  auto kprefetch = [&](int boff) {
+#pragma unroll
+    for (int i = 0; i < RING; ++i) kr[i] = kread(boff, i);
+  };
+
+  // scores of the tile in buffer boff into acc; `between(ks)` runs after the
+  // MFMAs of k-step ks
+  auto scores = [&](int boff, f32x4* acc, auto between) {
+    bf16x8 qx[KS - KQ][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 b0 = ks < KQ ? qf[0][ks] : qx[ks - KQ][0];
+      const bf16x8 b1 = ks < KQ ? qf[1][ks] : qx[ks - KQ][1];
+      const bf16x8 a_op = kr[ks % RING];
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks == 0) {
+        mfma16_first(acc[0], a_op, b0);
+        mfma16_first(acc[1], a_op, b1);
+      } else {
+        mfma16(acc[0], a_op, b0);
+        mfma16(acc[1], a_op, b1);
+      }
+      if (ks + RING < KS) kr[ks % RING] = kread(boff, ks + RING);
+      if (ks + QA >= KQ && ks + QA < KS) {
+        qx[ks + QA - KQ][0] = *(const MLA_LDS bf16x8*)(smem + qofs + 64 * (ks + QA - KQ));
+        qx[ks + QA - KQ][1] = *(const MLA_LDS bf16x8*)(smem + qofs + 64 * (ks + QA - KQ) + 16 * QR_ROW);
+      }
+      between(ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // first tile's scores and the segment's reference max
+  kprefetch(0);
+  scores(0, s0, [](int) {});
+  sync_scores();
+  {
+    const int nvalid = len - lt0 * TILE;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, 4 * q4 + rr < nvalid ? s0[hb][rr] * a.scale_log2 : -INFINITY);
+      mx = fmaxf(mx, shfl_xor(mx, ln, 16));
+      mx = fmaxf(mx, shfl_xor(mx, ln, 32));
+      m_ref[hb] = mx;
+    }
+  }
+  if (owner && ntiles > 1) kprefetch(TILE_BYTES);
+
+  // One pipeline step (tile it, scores in sc; scores of tile it+1 into sn).
+  auto step = [&](int it, f32x4* sc, f32x4* sn) {
+    const int boff = (it % NBUF) * TILE_BYTES;
+    const int nvalid = len - (lt0 + it) * TILE;  // positions < nvalid of this tile are visible
+    const bool pre = it + AHEAD < ntiles;        // tile it+AHEAD is loaded during this step
+    TileSrc ns = {nullptr, 0};
+    if (pre) {
+      ns = tile_src(a, b, (lt0 + it + AHEAD) * TILE, len);
+      // materialise the (possibly table-derived) source now: a scalar-load
+      // wait later would also drain the operand reads in flight
+      asm volatile("" : "+s"(ns.p), "+s"(ns.last));
+    }
+    const int nboff = ((it + AHEAD) % NBUF) * TILE_BYTES;
+
+    // ---- softmax of tile it: weights 2^(s - m_ref) (see the reference note
+    // below), two at a time, spread over the score MFMAs of tile it+1 when
+    // there is one. The denominator sums exactly the bf16 weights the value
+    // MFMAs use (a dot product of each rounded pair with (1, 1)).
+    bf16x2 pp[4];  // pair p: positions 4(l/16) + 2(p&1) + {0, 1} of head block p/2
+    // Positions past the visible length (last tile only) get weight 0: their
+    // rows repeat the last visible row, so their scores are finite and no
+    // larger than a visible one; the bf16 pairs are masked with keep[p & 1].
+    uint32_t keep[2] = {0xffffffffu, 0xffffffffu};
+    if (nvalid < TILE) {
+      const int lim = nvalid - 4 * q4;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        keep[h2] = (2 * h2 < lim ? 0xffffu : 0u) | (2 * h2 + 1 < lim ? 0xffff0000u : 0u);
+    }
+    auto soft2 = [&](int p) {
+      const int hb = p >> 1, r0 = 2 * (p & 1);
+      const float x0 = sc[hb][r0] * a.scale_log2 - m_ref[hb];
+      const float x1 = sc[hb][r0 + 1] * a.scale_log2 - m_ref[hb];
+      ovm = fmaxf(ovm, fmaxf(x0, x1));
+      float w0 = __builtin_amdgcn_exp2f(x0), w1 = __builtin_amdgcn_exp2f(x1);
+      opaque(w0);  // computed here, between the MFMAs, not where it is used
+      opaque(w1);
+      bf16x2 q;
+      q[0] = f32_to_bf16(w0);
+      q[1] = f32_to_bf16(w1);
+      q = __builtin_bit_cast(bf16x2, __builtin_bit_cast(uint32_t, q) & keep[p & 1]);
+      pp[p] = q;
+      const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+      lsum[hb] = __builtin_amdgcn_fdot2_f32_bf16(q, ones, lsum[hb], false);
+    };
+    if (owner) {
+      if (it + 1 < ntiles) {
+        scores(((it + 1) % NBUF) * TILE_BYTES, sn, [&](int ks) {
+          if ((ks & 3) == 1) soft2(ks >> 2);
+          if (pre && (ks & 3) == 0) load_tile(ns, nboff, ks >> 2);
+        });
+        sync_scores();
+      } else {
+#pragma unroll
+        for (int pi = 0; pi < 4; ++pi) soft2(pi);
+      }
+      const int pw = pwo + (it & 1) * P_BYTES;
+      *(MLA_LDS bf16x4*)(smem + pw) = __builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3);
+      *(MLA_LDS bf16x4*)(smem + pw + 16 * 32) = __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3);
+    } else if (pre) {
+#pragma unroll
+      for (int k = 0; k < 5; ++k) load_tile(ns, nboff, k);
+    }
+
+    // ---- V^T fragments of this wave's dims
+    s16x4 va[4], vb[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int xo = vx ^ (d << 6);
+      va[d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(smem + boff + vA + xo));
+      vb[d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(smem + boff + vB + xo));
+    }
+
+    // tile it+2 complete (published by this barrier); later tiles in flight
+    if (it + 2 < ntiles) {
+      const int after = ntiles - it - 3;  // tiles issued after it+2
+      if (after >= AHEAD - 2) {
+        if (wv < 2) wait_vmcnt<(AHEAD - 2) * 5>();
+        else wait_vmcnt<(AHEAD - 2) * 4>();
+      } else {
+        wait_vm(after * L);
+      }
+    }
+    wait_lgkm0();
+    block_barrier();  // weights of tile it and tile it+2 visible
+
+    // ---- weight fragments (B operand of 32x32x16: lane l holds head
+    // 32hb + l%32, positions 8(l/32) .. +7) and the first score operands of tile it+2
+    bf16x8 pf[NHB];
+    {
+      const int pr = pro + (it & 1) * P_BYTES;
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) pf[hb] = *(const MLA_LDS bf16x8*)(smem + pr + hb * 32 * 32);
+    }
+    if (owner && it + 2 < ntiles) kprefetch(((it + 2) % NBUF) * TILE_BYTES);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const s16x8 v8 = __builtin_shufflevector(va[d], vb[d], 0, 1, 2, 3, 4, 5, 6, 7);
+        o[hb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pf[hb], o[hb][d], 0, 0,
+                                                           0);
+      }
+  };
+  for (int it = 0; it < ntiles; ++it) {
+    step(it, s0, s1);
+    s0[0] = s1[0];
+    s0[1] = s1[1];
+  }
 
   // Softmax reference. Each head's reference max m_ref is the largest score
   // of the segment's first tile and the weights are 2^(x - m_ref). Keeping
   // the reference fixed keeps the output accumulator free of data-dependent
   // rescaling (a conditional rescale moves it out of the accumulation
   // registers). If a later score exceeds m_ref by more than SLACK the
-  // exponent is clamped and the row is flagged; a fix-up pass recomputes
-  // flagged rows with the generic kernel. Scores would have to grow by more
-  // than 2^64 within one segment for that to happen.
-  float m_ref = -INFINITY;
-  float l_run = 0.f;  // running denominator over this lane's half of the positions
-  f32x16 o[16];
+  // exponent is clamped and the row is flagged; the first workgroup to flag
+  // row r recomputes the whole row with the generic running-max kernel into
+  // the final output, and the combine skips flagged rows. Scores would have
+  // to grow by more than 2^64 within one segment for that to happen.
+  int le = lane;  // per-lane values of the epilogue stay here (see the tile loop)
+  opaque(le);
+  float lse_v[2] = {0.f, 0.f};
+  if (owner) {
+    if (__any(ovm > SLACK) && le == 0) atomicOr(seg_flag, 1);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) o[i] = f32x16{};
-  bool overflow = false;
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + NSTAGE - 2 < ntiles) wait_vmcnt<(NSTAGE - 2) * LPW>();
-    else wait_vmcnt<0>();
-    block_barrier();  // tile it visible; tile it-1's buffer free for reuse
-    if (it + NSTAGE - 1 < ntiles)
-      issue_tile(a, smem + ((it + NSTAGE - 1) % NSTAGE) * TILE_BYTES, b, (lt0 + it + NSTAGE - 1) * TILE, len,
-                 lane, wv);
-    const char* buf = smem + (it % NSTAGE) * TILE_BYTES;
-    const int t0 = (lt0 + it) * TILE;
-
-    // Per-lane LDS offsets, rebuilt every tile from an opaque copy of the lane
-    // id: values live across the loop get spilled, and a spill reload in front
-    // of the loop makes the compiler wait for all in-flight tile loads.
-    // Forms are base + 32 * (j ^ x) (QK) and base + 64 * (u ^ x) (PV); the
-    // remaining terms are immediates.
-    int ln = lane;
-    opaque(ln);
-    const int mrow = ln & 31;  // QK: this lane's A-operand row (position) and head row
-    const int sCm = sC(mrow), sRm = sR(mrow);
-    const int gg = ln >> 5;
-    const int baseC = mrow * 1024 + ((gg ^ (sCm & 1)) << 4);
-    const int baseR = C_BYTES + mrow * 128 + ((gg ^ (sRm & 1)) << 4);
-    const int baseQ = mrow * QL_ROW + ((gg ^ (sRm & 1)) << 4);
-    const int xC = sCm >> 1, xR = sRm >> 1;
-    const int q16 = ln & 15;
-    const int rowA = 4 * gg + (q16 >> 2);  // PV: rows of the first transposing load (k-step 0)
-    const int rowB = rowA + 8;
-    const int cb = 2 * ((ln >> 4) & 1) + ((q16 & 3) >> 1);
-    const int sA = sC(rowA), sB = sC(rowB);
-    const int baseA = rowA * 1024 + ((cb ^ (sA & 3)) << 4) + (q16 & 1) * 8;
-    const int baseB = rowB * 1024 + ((cb ^ (sB & 3)) << 4) + (q16 & 1) * 8;
-    const int xA = sA >> 2, xB = sB >> 2;
-
-    // ---- S^T[position][head] = K_tile . Q^T, 36 k-steps of 16 dims. LDS
-    // operands are read RING k-steps ahead of their MFMA; the compiler
-    // barriers keep reads in this order (neither hoisted nor sunk).
-    f32x16 sacc;
-    {
-      // A operand (K tile rows) of k-step ks
-      auto kread = [&](int ks) -> bf16x8 {
-        const char* p = ks < 32 ? buf + baseC + (((ks & 7) ^ xC) << 5) + 256 * (ks >> 3)
-                                : buf + baseR + (((ks - 32) ^ xR) << 5);
-        return *(const MLA_LDS bf16x8*)p;
-      };
-      // B operand of k-steps ks >= KQR (query dims kept in LDS)
-      auto qread = [&](int ks) -> bf16x8 {
-        const int kq = ks - KQR;
-        return *(const MLA_LDS bf16x8*)(ql + baseQ + 128 * (kq >> 2) + (((kq & 3) ^ xR) << 5));
-      };
-      bf16x8 kr[RING], qr[RING];
-#pragma unroll
-      for (int i = 0; i < RING; ++i) {
-        kr[i] = kread(i);
-        if (i >= KQR) qr[i] = qread(i);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 36; ++ks) {
-        const bf16x8 a_op = kr[ks % RING];
-        const bf16x8 b_op = ks < KQR ? qf[ks] : qr[ks % RING];
-        if (ks + RING < 36) {
-          kr[ks % RING] = kread(ks + RING);
-          if (ks + RING >= KQR) qr[ks % RING] = qread(ks + RING);
-        }
-        asm volatile("" ::: "memory");
-        if (ks == 0) mfma_vacc_first(sacc, a_op, b_op);
-        else mfma_vacc(sacc, a_op, b_op);
-      }
-    }
-    // the last QK MFMA's result is read by VALU next: 8-pass XDL -> VALU read
-    // needs 11 wait states (the asm MFMA is invisible to the hazard checker)
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
-
-    // ---- softmax weights (lane = head; 16 positions here, 16 in lane^32)
-    const int nvalid = len - t0;  // positions i < nvalid are visible
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int i = 8 * (rr >> 2) + 4 * g + (rr & 3);
-      tmax = fmaxf(tmax, i < nvalid ? sacc[rr] * a.scale_log2 : -INFINITY);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    m_ref = m_ref == -INFINITY ? tmax : m_ref;  // first tile of the segment
-    overflow |= tmax > m_ref + SLACK;
-    bf16x8 pb[2];
-    float psum = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int i = 8 * (rr >> 2) + 4 * g + (rr & 3);
-      const float e = fminf(sacc[rr] * a.scale_log2 - m_ref, SLACK);
-      const bf16 p = f32_to_bf16(i < nvalid ? __builtin_amdgcn_exp2f(e) : 0.f);
-      pb[rr >> 3][rr & 7] = p;
-      psum += bf16_to_f32(p);  // the denominator sums exactly the weights the MFMA uses
-    }
-    l_run += psum;
-
-    // ---- O^T[dim][head] += V^T . P^T ; V^T fragments via transposing LDS loads.
-    // Slot s of k-step kk holds position 16kk + 8(s/4) + 4g + s%4 (the order of
-    // the S accumulators): lane group (l/16) reads positions 16kk + 4g + {0..3}
-    // and the same +8, 16 dims each.
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    // 32 PV steps j = 16 kk + db; transposing reads run RING steps ahead
-    auto vread = [&](int j, bool second) -> s16x4 {
-      const int kk = j >> 4, db = j & 15;
-      const char* p = buf + (second ? baseB + (((db & 3) ^ xB) << 6) : baseA + (((db & 3) ^ xA) << 6)) +
-                      256 * (db >> 2) + kk * 16 * 1024;
-      return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)p);
-    };
-    s16x4 va[RING], vb[RING];
-#pragma unroll
-    for (int i = 0; i < RING; ++i) {
-      va[i] = vread(i, false);
-      vb[i] = vread(i, true);
-    }
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const s16x8 v8 = __builtin_shufflevector(va[j % RING], vb[j % RING], 0, 1, 2, 3, 4, 5, 6, 7);
-      if (j + RING < 32) {
-        va[j % RING] = vread(j + RING, false);
-        vb[j % RING] = vread(j + RING, true);
-      }
-      asm volatile("" ::: "memory");
-      o[j & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pb[j >> 4], o[j & 15], 0, 0, 0);
+    for (int hb = 0; hb < 2; ++hb) {
+      float l = lsum[hb];
+      l += shfl_xor(l, le, 16);
+      l += shfl_xor(l, le, 32);
+      lse_v[hb] = (m_ref[hb] + __log2f(l)) * kLn2;
+      if (le < 16) inv_s[wv * 32 + hb * 16 + le] = 1.0f / l;
     }
   }
-  // Overflow of the fixed reference (see above): the first workgroup to flag
-  // row r recomputes the whole row with the generic running-max kernel into
-  // the final output; the combine skips flagged rows.
-  if (active && __any(overflow) && lane == 0) atomicOr(seg_flag, 1);
-  block_barrier();
+  __syncthreads();
   if (*seg_flag) {
     __shared__ int claim;
     if (threadIdx.x == 0) claim = atomicOr(a.pl.flags + r, 1) == 0;
@@ -606,45 +808,57 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
     if (claim) recompute_row(a, r, smem);
     return;
   }
-  if (!active) return;
 
-  // ---- finish: full denominator, normalise, write final or partial result
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
-  const float lse_v = (m_ref + __log2f(l_tot)) * kLn2;
-  if (full) {
-    bf16* orow = a.out + ((size_t)r * H + h) * DC;
+  // ---- finish: normalise, write final (bf16) or partial (fp32) result
+  if (owner && le < 16) {
 #pragma unroll
-    for (int db = 0; db < 16; ++db)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        bf16x4 v;
-        v[0] = f32_to_bf16(o[db][4 * rq + 0] * inv);
-        v[1] = f32_to_bf16(o[db][4 * rq + 1] * inv);
-        v[2] = f32_to_bf16(o[db][4 * rq + 2] * inv);
-        v[3] = f32_to_bf16(o[db][4 * rq + 3] * inv);
-        *(bf16x4*)(orow + db * 32 + 8 * rq + 4 * g) = v;
+    for (int hb = 0; hb < 2; ++hb) {
+      const int h = wv * 32 + hb * 16 + le;
+      if (full) {
+        if (a.lse) a.lse[(size_t)r * H + h] = lse_v[hb];
+      } else {
+        a.pl.part_lse[(size_t)slot * H + h] = lse_v[hb];
       }
-    if (a.lse && g == 0) a.lse[(size_t)r * H + h] = lse_v;
-  } else {
-    float* prow = a.pl.part_o + ((size_t)slot * H + h) * DC;
+    }
+  }
+  const int g = le >> 5;
 #pragma unroll
-    for (int db = 0; db < 16; ++db)
+  for (int hb = 0; hb < NHB; ++hb) {
+    const int hh = 32 * hb + (le & 31);
+    const float inv = inv_s[hh];
+    if (full) {
+      bf16* orow = a.out + ((size_t)r * H + hh) * DC + DW * wv;
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        f32x4 v;
-        v[0] = o[db][4 * rq + 0] * inv;
-        v[1] = o[db][4 * rq + 1] * inv;
-        v[2] = o[db][4 * rq + 2] * inv;
-        v[3] = o[db][4 * rq + 3] * inv;
-        *(f32x4*)(prow + db * 32 + 8 * rq + 4 * g) = v;
-      }
-    if (g == 0) a.pl.part_lse[(size_t)slot * H + h] = lse_v;
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          bf16x4 v;
+          v[0] = f32_to_bf16(o[hb][d][4 * rq + 0] * inv);
+          v[1] = f32_to_bf16(o[hb][d][4 * rq + 1] * inv);
+          v[2] = f32_to_bf16(o[hb][d][4 * rq + 2] * inv);
+          v[3] = f32_to_bf16(o[hb][d][4 * rq + 3] * inv);
+          *(bf16x4*)(orow + d * 32 + 8 * rq + 4 * g) = v;
+        }
+    } else {
+      float* prow = a.pl.part_o + ((size_t)slot * H + hh) * DC + DW * wv;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          f32x4 v;
+          v[0] = o[hb][d][4 * rq + 0] * inv;
+          v[1] = o[hb][d][4 * rq + 1] * inv;
+          v[2] = o[hb][d][4 * rq + 2] * inv;
+          v[3] = o[hb][d][4 * rq + 3] * inv;
+          *(f32x4*)(prow + d * 32 + 8 * rq + 4 * g) = v;
+        }
+    }
   }
 }
 
+template <int NHB>
 __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(Args a) {
-  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * TILE_BYTES + QL_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   __shared__ int seg_flag;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -655,13 +869,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(Args a) {
   const int t_begin = w * per;
   if (t_begin >= total) return;
   const int t_end = min(t_begin + per, total);
-  for (int r = plan_row_of(a.pl.cum, a.pl.R, t_begin); r < a.pl.R; ++r) {
+  for (int r = a.pl.wrow[w]; r < a.pl.R; ++r) {
     const int c0 = a.pl.cum[r], c1 = a.pl.cum[r + 1];
     if (c0 >= t_end) break;
     if (c1 <= t_begin || c1 == c0) continue;
     const int lt0 = max(t_begin, c0) - c0, lt1 = min(t_end, c1) - c0;
     const bool full = c0 >= t_begin && c1 <= t_end;
-    attend_segment(a, r, lt0, lt1, full, plan_slot(w, c0, per), smem, &seg_flag, lane, wv);
+    attend_segment<NHB>(a, r, lt0, lt1, full, plan_slot(w, c0, per), smem, &seg_flag, lane, wv);
   }
 }
 }  // namespace mf
@@ -844,7 +1058,12 @@ static int launch_attention_t(const AttnCall& c) {
     a.scale_log2 = c.kq_scale * kLog2e;
     a.out = (bf16*)c.out;
     a.lse = c.lse;
-    hipLaunchKernelGGL(mf::attn_mfma_kernel, dim3(c.G), dim3(mf::NW * 64), 0, c.stream, a);
+    switch (c.H / 32) {
+      case 1: hipLaunchKernelGGL(mf::attn_mfma_kernel<1>, dim3(c.G), dim3(mf::NW * 64), 0, c.stream, a); break;
+      case 2: hipLaunchKernelGGL(mf::attn_mfma_kernel<2>, dim3(c.G), dim3(mf::NW * 64), 0, c.stream, a); break;
+      case 3: hipLaunchKernelGGL(mf::attn_mfma_kernel<3>, dim3(c.G), dim3(mf::NW * 64), 0, c.stream, a); break;
+      default: hipLaunchKernelGGL(mf::attn_mfma_kernel<4>, dim3(c.G), dim3(mf::NW * 64), 0, c.stream, a); break;
+    }
   } else {
     launch_generic<T>(c, pl);
   }

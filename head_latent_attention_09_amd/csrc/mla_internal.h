@@ -16,6 +16,7 @@ namespace mla {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -54,6 +55,7 @@ struct Plan {
   int32_t* len;     // [R]: visible positions per row (clamped)
   int32_t* flags;   // [R]: set when a row had to be recomputed (see the attention kernel)
   int32_t* split;   // [1 + G]: count, then the rows cut by a worker boundary
+  int32_t* wrow;    // [G]: first row of every worker that has tiles
   float* part_o;    // [2G, H, d_c]
   float* part_lse;  // [2G, H]
   int R;
@@ -63,11 +65,12 @@ struct Plan {
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// workspace layout: cum | len | flags | split | part_o | part_lse
+// workspace layout: cum | len | flags | split | wrow | part_o | part_lse
 inline size_t plan_bytes(int64_t R, int G, int H, int d_c) {
   size_t b = align256(sizeof(int32_t) * (size_t)(R + 1));
   b += 2 * align256(sizeof(int32_t) * (size_t)R);
   b += align256(sizeof(int32_t) * (size_t)(G + 1));
+  b += align256(sizeof(int32_t) * (size_t)G);
   b += align256(sizeof(float) * (size_t)2 * G * H * d_c);
   b += align256(sizeof(float) * (size_t)2 * G * H);
   return b;
@@ -84,6 +87,8 @@ inline Plan plan_layout(void* ws, int R, int G, int H, int d_c, int tile) {
   p += align256(sizeof(int32_t) * (size_t)R);
   pl.split = (int32_t*)p;
   p += align256(sizeof(int32_t) * (size_t)(G + 1));
+  pl.wrow = (int32_t*)p;
+  p += align256(sizeof(int32_t) * (size_t)G);
   pl.part_o = (float*)p;
   p += align256(sizeof(float) * (size_t)2 * G * H * d_c);
   pl.part_lse = (float*)p;
@@ -104,16 +109,6 @@ __device__ __forceinline__ int plan_per_worker(int total, int G) {
 __device__ __forceinline__ int xcd_worker(int bx, int G) {
   if (G % 8 != 0) return bx;
   return (bx % 8) * (G / 8) + bx / 8;
-}
-
-// first row whose tiles contain global tile t (cum[row] <= t < cum[row+1])
-__device__ __forceinline__ int plan_row_of(const int32_t* cum, int R, int t) {
-  int lo = 0, hi = R - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (cum[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
 }
 
 __device__ __forceinline__ int plan_slot(int w, int row_start_tile, int per_worker) {
