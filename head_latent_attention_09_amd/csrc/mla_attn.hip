@@ -227,7 +227,7 @@ __device__ void attend_segment(const Args<T>& a, int r, int lt0, int lt1, bool f
       if (d < d_c) {
         float v = acc[hh][k] * stat_s[hh];
         if (full) store_f32(a.out + ((size_t)r * H + h) * d_c + d, v);
-        else a.pl.part_o[((size_t)slot * H + h) * d_c + d] = v;
+        else store_f32((T*)a.pl.part_o + ((size_t)slot * H + h) * d_c + d, v);
       }
     }
     if (tid == 0) {
@@ -840,17 +840,17 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
           *(bf16x4*)(orow + d * 32 + 8 * rq + 4 * g) = v;
         }
     } else {
-      float* prow = a.pl.part_o + ((size_t)slot * H + hh) * DC + DW * wv;
+      bf16* prow = (bf16*)a.pl.part_o + ((size_t)slot * H + hh) * DC + DW * wv;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          f32x4 v;
-          v[0] = o[hb][d][4 * rq + 0] * inv;
-          v[1] = o[hb][d][4 * rq + 1] * inv;
-          v[2] = o[hb][d][4 * rq + 2] * inv;
-          v[3] = o[hb][d][4 * rq + 3] * inv;
-          *(f32x4*)(prow + d * 32 + 8 * rq + 4 * g) = v;
+          bf16x4 v;
+          v[0] = f32_to_bf16(o[hb][d][4 * rq + 0] * inv);
+          v[1] = f32_to_bf16(o[hb][d][4 * rq + 1] * inv);
+          v[2] = f32_to_bf16(o[hb][d][4 * rq + 2] * inv);
+          v[3] = f32_to_bf16(o[hb][d][4 * rq + 3] * inv);
+          *(bf16x4*)(prow + d * 32 + 8 * rq + 4 * g) = v;
         }
     }
   }
@@ -886,8 +886,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(Args a) {
 // Merge n normalised partial results of one (row, head): lse = log sum e^lse_p,
 // out = sum_p e^(lse_p - lse) o_p. Parts with lse_p = -inf are skipped (never
 // read). Threads of the block split d_c.
+template <typename PT>
 struct PartRef {
-  const float* o;
+  const PT* o;
   float lse;
 };
 
@@ -902,7 +903,7 @@ __device__ void combine_head(int n, PartFn part, int d_c, OutT* out, float* lse_
       if (pp.lse == -INFINITY) continue;
       const float e = __expf(pp.lse - mx);
       wsum += e;
-      acc += e * pp.o[d];
+      acc += e * load_f32(pp.o + d);
     }
     store_f32(out + d, wsum > 0.f ? acc / wsum : 0.f);
   }
@@ -940,7 +941,7 @@ __global__ __launch_bounds__(256) void plan_combine_kernel(Plan pl, int H, int d
       const int h = h0 + hh;
       auto part = [&](int i) {
         const int slot = plan_slot(w0 + i, c0, per);
-        return PartRef{pl.part_o + ((size_t)slot * H + h) * d_c, pl.part_lse[(size_t)slot * H + h]};
+        return PartRef<OutT>{(const OutT*)pl.part_o + ((size_t)slot * H + h) * d_c, pl.part_lse[(size_t)slot * H + h]};
       };
       combine_head<OutT>(n, part, d_c, out + ((size_t)r * H + h) * d_c, lse ? lse + (size_t)r * H + h : nullptr);
       __syncthreads();
@@ -970,7 +971,7 @@ __global__ __launch_bounds__(256) void plan_combine_kernel(Plan pl, int H, int d
       f32x4 acc = f32x4{};
       for (int i = 0; i < n; ++i) {
         const int slot = plan_slot(w0 + i, c0, per);
-        const f32x4 v = *(const f32x4*)(pl.part_o + ((size_t)slot * H + h) * d_c + d);
+        const f32x4 v = load4_f32((const OutT*)pl.part_o + ((size_t)slot * H + h) * d_c + d);
         acc += w_s[hh][i] * v;
       }
       OutT* o = out + ((size_t)r * H + h) * d_c + d;
@@ -986,7 +987,7 @@ __global__ __launch_bounds__(256) void plan_combine_kernel(Plan pl, int H, int d
       const int h = h0 + hh;
       float acc = 0.f;
       for (int i = 0; i < n; ++i)
-        acc += w_s[hh][i] * pl.part_o[((size_t)plan_slot(w0 + i, c0, per) * H + h) * d_c + d];
+        acc += w_s[hh][i] * load_f32((const OutT*)pl.part_o + ((size_t)plan_slot(w0 + i, c0, per) * H + h) * d_c + d);
       store_f32(out + ((size_t)r * H + h) * d_c + d, acc * inv_s[hh]);
     }
   }
@@ -999,7 +1000,7 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(const float* o_parts, 
   const int h = blockIdx.y;
   auto part = [&](int p) {
     const size_t idx = ((size_t)p * rows + r) * H + h;
-    return PartRef{o_parts + idx * d_c, lse_parts[idx]};
+    return PartRef<float>{o_parts + idx * d_c, lse_parts[idx]};
   };
   combine_head<OutT>(n, part, d_c, out + ((size_t)r * H + h) * d_c, lse ? lse + (size_t)r * H + h : nullptr);
 }

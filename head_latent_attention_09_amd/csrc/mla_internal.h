@@ -32,6 +32,13 @@ __device__ __forceinline__ bf16 f32_to_bf16(float x) { return (bf16)x; }  // nea
 template <typename T> __device__ __forceinline__ float load_f32(const T* p);
 template <> __device__ __forceinline__ float load_f32<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float load_f32<bf16>(const bf16* p) { return (float)*p; }
+// four consecutive elements (16-byte aligned for fp32, 8-byte for bf16) as fp32
+template <typename T> __device__ __forceinline__ f32x4 load4_f32(const T* p);
+template <> __device__ __forceinline__ f32x4 load4_f32<float>(const float* p) { return *(const f32x4*)p; }
+template <> __device__ __forceinline__ f32x4 load4_f32<bf16>(const bf16* p) {
+  const bf16x4 v = *(const bf16x4*)p;
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
 template <typename T> __device__ __forceinline__ void store_f32(T* p, float v);
 template <> __device__ __forceinline__ void store_f32<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void store_f32<bf16>(bf16* p, float v) { *p = (bf16)v; }
@@ -56,7 +63,7 @@ struct Plan {
   int32_t* flags;   // [R]: set when a row had to be recomputed (see the attention kernel)
   int32_t* split;   // [1 + G]: count, then the rows cut by a worker boundary
   int32_t* wrow;    // [G]: first row of every worker that has tiles
-  float* part_o;    // [2G, H, d_c]
+  float* part_o;    // [2G, H, d_c] partial outputs, stored in the call's dtype (bf16 calls use half the region)
   float* part_lse;  // [2G, H]
   int R;
   int G;
