@@ -963,7 +963,26 @@ __global__ __launch_bounds__(256) void plan_combine_kernel(Plan pl, int H, int d
     if (lse) lse[(size_t)r * H + h] = mx + __logf(ws);
   }
   __syncthreads();
-  if ((d_c & 3) == 0) {
+  if (sizeof(OutT) == 2 && (d_c & 7) == 0 && ((uintptr_t)out & 15) == 0) {  // bf16: 16-byte loads and stores
+    const int q8 = d_c >> 3;
+    for (int idx = threadIdx.x; idx < nh * q8; idx += blockDim.x) {
+      const int hh = idx / q8, d = (idx - hh * q8) * 8;
+      const int h = h0 + hh;
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < n; ++i) {
+        const int slot = plan_slot(w0 + i, c0, per);
+        const bf16x8 v = *(const bf16x8*)((const bf16*)pl.part_o + ((size_t)slot * H + h) * d_c + d);
+        const float wgt = w_s[hh][i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += wgt * (float)v[j];
+      }
+      const float sc = inv_s[hh];
+      bf16x8 o8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o8[j] = f32_to_bf16(acc[j] * sc);
+      *(bf16x8*)((bf16*)out + ((size_t)r * H + h) * d_c + d) = o8;
+    }
+  } else if ((d_c & 3) == 0) {
     const int q4 = d_c >> 2;
     for (int idx = threadIdx.x; idx < nh * q4; idx += blockDim.x) {
       const int hh = idx / q4, d = (idx - hh * q4) * 4;
