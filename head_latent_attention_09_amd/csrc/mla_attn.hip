@@ -809,7 +809,7 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
     return;
   }
 
-  // ---- finish: normalise, write final (bf16) or partial (fp32) result
+  // ---- finish: normalise, write the final row or this worker's partial (bf16)
   if (owner && le < 16) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {

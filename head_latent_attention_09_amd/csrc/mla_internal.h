@@ -52,8 +52,9 @@ template <> __device__ __forceinline__ void store_f32<bf16>(bf16* p, float v) { 
 // and dealt out in equal contiguous ranges of `per_worker` tiles to G
 // workers (one workgroup each). A worker's range is a run of segments, one
 // per row it touches. A row entirely inside one worker is finished by that
-// worker; a row cut by worker boundaries leaves one fp32 partial result
-// (normalised output + lse) per touching worker, merged by the combine.
+// worker; a row cut by worker boundaries leaves one partial result
+// (normalised output in the call's dtype + fp32 lse) per touching worker,
+// merged by the combine.
 // Partial slot of (worker w, row r): 2w if r started before w's range
 // (r is w's first segment), else 2w + 1 (r runs past w's end). So 2G slots.
 // ---------------------------------------------------------------------------
