@@ -159,6 +159,96 @@ __global__ __launch_bounds__(NT, 2) void gemm_mfma_kernel(Args a) {
     }
   }
 }
+
+// ---------------------------------------------------------------------------
+// Small-row-count up-projection (decode: one row per sequence). The 128x128
+// tiles above leave most compute units idle when N is small (N=64, H=128 is
+// 128 workgroups), and their two-stage pipeline keeps only one 64-wide K
+// slice in flight per workgroup. Here a workgroup owns a 64-row x 64-column
+// tile with the whole K extent resident in LDS (NS slices of 64; 128 KiB at
+// K=512): every load of the tile is issued up front, and slice s is consumed
+// as soon as its loads have landed. Wave (wm, wn) computes rows 32wm..,
+// columns 32wn.. with one 32x32x16 MFMA per 16-wide k-step.
+// Workgroups are numbered so that the column blocks of one (row block, head)
+// run on the same XCD (the dispatcher deals workgroups to the 8 XCDs round
+// robin), where they share the A rows in L2.
+// ---------------------------------------------------------------------------
+constexpr int SM = 64, SN = 64;
+constexpr int S_SLICE = (SM + SN) * BK * 2;  // 16 KiB per 64-wide K slice
+
+template <int NS>
+__global__ __launch_bounds__(NT, 1) void upv_resident_kernel(Args a, int ncb, int units) {
+  __shared__ __attribute__((aligned(1024))) char smem[NS * S_SLICE];
+  const int L = blockIdx.x;
+  const int unit = (L / (8 * ncb)) * 8 + (L & 7);  // (row block, head)
+  if (unit >= units) return;
+  const int cb = (L >> 3) % ncb;
+  const int h = unit % a.H;
+  const int64_t n0 = (int64_t)(unit / a.H) * SM;
+  const int j0 = cb * SN;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = lane >> 5;
+  const int wm = wv >> 1, wn = wv & 1;
+
+  // loads: per slice 8 of A (64 rows x 8 chunks) and 8 of W, two of each per wave
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+    char* st = smem + sl * S_SLICE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ld = wv * 2 + i;
+      const int p = ld * 64 + lane;
+      const int row = p >> 3;
+      const int c = (p & 7) ^ swz8(row);
+      int64_t n = n0 + row;
+      n = n < a.N ? n : a.N - 1;
+      __builtin_amdgcn_global_load_lds((const void*)(a.A + ((size_t)n * a.H + h) * a.K + sl * BK + c * 8),
+                                       (MLA_LDS void*)(st + ld * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ld = wv * 2 + i;
+      const int p = ld * 64 + lane;
+      const int row = p >> 3;
+      const int c = (p & 7) ^ swz8(row);
+      __builtin_amdgcn_global_load_lds((const void*)(a.W + ((size_t)h * a.D + j0 + row) * a.K + sl * BK + c * 8),
+                                       (MLA_LDS void*)(st + SM * 128 + ld * 1024), 16, 0, 0);
+    }
+  }
+
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+    // this wave's loads of slices 0..sl have landed (4 per slice, issued in order)
+    switch (NS - 1 - sl) {  // a constant once the loop is unrolled
+#define MLA_VM(K_)                                                                   \
+  case K_:                                                                         \
+    __builtin_amdgcn_s_waitcnt(((4 * K_) & 15) | (((4 * K_) >> 4) << 14) | (7 << 4) | (15 << 8)); \
+    break;
+      MLA_VM(0) MLA_VM(1) MLA_VM(2) MLA_VM(3) MLA_VM(4) MLA_VM(5) MLA_VM(6) MLA_VM(7)
+#undef MLA_VM
+    }
+    barrier();  // ... and every other wave's
+    const char* sa = smem + sl * S_SLICE;
+    const char* sb = sa + SM * 128;
+    const int ra = wm * 32 + (lane & 31), rb = wn * 32 + (lane & 31);
+    bf16x8 af[BK / 16], bfr[BK / 16];  // all fragments of the slice first: one LDS latency per slice
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      af[ks] = *(const MLA_LDS bf16x8*)(sa + ra * 128 + (((2 * ks + g) ^ swz8(ra)) * 16));
+      bfr[ks] = *(const MLA_LDS bf16x8*)(sb + rb * 128 + (((2 * ks + g) ^ swz8(rb)) * 16));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], bfr[ks], acc, 0, 0, 0);
+  }
+  const int col = j0 + wn * 32 + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t n = n0 + wm * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+    if (n < a.N) a.out[((size_t)n * a.H + h) * a.ldo + col] = f32_to_bf16(acc[r]);
+  }
+}
 }  // namespace gm
 
 // generic per-head product: one thread per output element, fp32 accumulation
@@ -238,6 +328,22 @@ int launch_up_v(const void* lat, const void* w_uv, void* out, int64_t N, int H, 
                 hipStream_t s) {
   if (dtype == MLA_BF16 && mfma_ok(d_c, d_v, d_v, lat, w_uv, out)) {
     gm::Args a{(const bf16*)lat, (const bf16*)w_uv, (bf16*)out, nullptr, N, H, d_c, d_v, d_v, 0};
+    const int64_t big_tiles = (N + gm::BM - 1) / gm::BM * (d_v / gm::BN) * H;
+    const int ns = d_c / gm::BK;
+    if (big_tiles < 512 && ns <= 8) {  // too few 128x128 tiles to fill the chip: 64x64, K resident
+      const int ncb = d_v / gm::SN;
+      const int64_t units = (N + gm::SM - 1) / gm::SM * H;
+      const unsigned blocks = (unsigned)((units + 7) / 8 * 8 * ncb);
+      switch (ns) {
+#define MLA_UPV(NS_)                                                                              \
+  case NS_:                                                                                     \
+    hipLaunchKernelGGL(gm::upv_resident_kernel<NS_>, dim3(blocks), dim3(gm::NT), 0, s, a, ncb, (int)units); \
+    break;
+        MLA_UPV(1) MLA_UPV(2) MLA_UPV(3) MLA_UPV(4) MLA_UPV(5) MLA_UPV(6) MLA_UPV(7) MLA_UPV(8)
+#undef MLA_UPV
+      }
+      return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+    }
     dim3 grid((unsigned)((N + gm::BM - 1) / gm::BM), d_v / gm::BN, H);
     hipLaunchKernelGGL(gm::gemm_mfma_kernel<true>, grid, dim3(gm::NT), 0, s, a);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
