@@ -62,7 +62,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(RowMap m, Plan pl, int H, in
   for (int r = r0; r < r1; ++r) {
     const int n = (pl.len[r] + tile - 1) / tile;
     pl.cum[r] = base;
-    if (n > 0 && base / per != (base + n - 1) / per) pl.split[1 + atomicAdd(&nsplit, 1)] = r;
+    if (n > 0 && base / per != (base + n - 1) / per) {
+      const int w0 = base / per;
+      *(int4*)(pl.split + 4 + 4 * atomicAdd(&nsplit, 1)) =
+          int4{r, plan_slot(w0, base, per), w0, (base + n - 1) / per - w0 + 1};
+    }
     // workers whose range starts inside this row's tiles begin with this row
     for (int w = (base + per - 1) / per; n > 0 && w * per < base + n && w < pl.G; ++w) pl.wrow[w] = r;
     base += n;
@@ -917,99 +921,70 @@ __device__ void combine_head(int n, PartFn part, int d_c, OutT* out, float* lse_
   }
 }
 
-// Split rows: workgroup (k, hb) merges heads 8hb .. 8hb+7 of the k-th row of
-// the plan's split list from its partial slots (one per worker it spans).
-// Rows the attention kernel recomputed (flagged) are already final.
-constexpr int CHB = 8;  // heads per combine workgroup
-template <typename OutT>
+// Split rows: workgroup (x, k) merges items 256x .. 256x+255 of the k-th row
+// of the plan's split list, an item being VEC consecutive dims of one head
+// (16 bytes of the output). The list entry gives the row and its parts: part
+// 0 in slot s0, part i > 0 in slot 2(w0 + i) (the row started before those
+// workers' ranges). Each thread issues the lse and partial loads of up to NP
+// parts at once, then merges them with a running maximum, so a workgroup
+// waits for memory twice (list entry, then data). Rows the attention kernel
+// recomputed (flagged) are already final.
+template <typename OutT, int VEC>
 __global__ __launch_bounds__(256) void plan_combine_kernel(Plan pl, int H, int d_c, OutT* out, float* lse) {
-  __shared__ float w_s[CHB][64];
-  __shared__ float inv_s[CHB];
-  const int k = blockIdx.x;
+  constexpr int NP = 4;
+  typedef OutT vec_t __attribute__((ext_vector_type(VEC)));
+  const int k = blockIdx.y;
+  const int4 e = *(const int4*)(pl.split + 4 + 4 * k);
   if (k >= pl.split[0]) return;
-  const int r = pl.split[1 + k];
-  if (pl.flags[r]) return;
-  const int total = pl.cum[pl.R];
-  const int per = plan_per_worker(total, pl.G);
-  const int c0 = pl.cum[r], c1 = pl.cum[r + 1];
-  const int w0 = c0 / per;
-  const int n = (c1 - 1) / per - w0 + 1;
-  const int h0 = blockIdx.y * CHB;
-  const int nh = min(CHB, H - h0);
-  if (n > 64) {  // very long rows: one head at a time
-    for (int hh = 0; hh < nh; ++hh) {
-      const int h = h0 + hh;
-      auto part = [&](int i) {
-        const int slot = plan_slot(w0 + i, c0, per);
-        return PartRef<OutT>{(const OutT*)pl.part_o + ((size_t)slot * H + h) * d_c, pl.part_lse[(size_t)slot * H + h]};
-      };
-      combine_head<OutT>(n, part, d_c, out + ((size_t)r * H + h) * d_c, lse ? lse + (size_t)r * H + h : nullptr);
-      __syncthreads();
-    }
-    return;
-  }
-  // weights e^(lse_i - lse) per (part, head), normalised
-  if (threadIdx.x < nh) {
-    const int h = h0 + threadIdx.x;
-    float mx = -INFINITY;
-    for (int i = 0; i < n; ++i) mx = fmaxf(mx, pl.part_lse[(size_t)plan_slot(w0 + i, c0, per) * H + h]);
-    float ws = 0.f;
-    for (int i = 0; i < n; ++i) {
-      const float e = __expf(pl.part_lse[(size_t)plan_slot(w0 + i, c0, per) * H + h] - mx);
-      w_s[threadIdx.x][i] = e;
-      ws += e;
-    }
-    inv_s[threadIdx.x] = 1.0f / ws;
-    if (lse) lse[(size_t)r * H + h] = mx + __logf(ws);
-  }
-  __syncthreads();
-  if (sizeof(OutT) == 2 && (d_c & 7) == 0 && ((uintptr_t)out & 15) == 0) {  // bf16: 16-byte loads and stores
-    const int q8 = d_c >> 3;
-    for (int idx = threadIdx.x; idx < nh * q8; idx += blockDim.x) {
-      const int hh = idx / q8, d = (idx - hh * q8) * 8;
-      const int h = h0 + hh;
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int i = 0; i < n; ++i) {
-        const int slot = plan_slot(w0 + i, c0, per);
-        const bf16x8 v = *(const bf16x8*)((const bf16*)pl.part_o + ((size_t)slot * H + h) * d_c + d);
-        const float wgt = w_s[hh][i];
+  const int r = e.x, s0 = e.y, w0 = e.z, n = e.w;
+  const int nq = d_c / VEC;
+  const int item = blockIdx.x * 256 + threadIdx.x;
+  if (item >= H * nq) return;
+  const int h = item / nq, d = (item - h * nq) * VEC;
+  const int flagged = pl.flags[r];
+  float mx = -INFINITY, ws = 0.f;
+  float acc[VEC];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] += wgt * (float)v[j];
-      }
-      const float sc = inv_s[hh];
-      bf16x8 o8;
+  for (int x = 0; x < VEC; ++x) acc[x] = 0.f;
+  for (int p0 = 0; p0 < n; p0 += NP) {
+    float l[NP];
+    vec_t v[NP];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o8[j] = f32_to_bf16(acc[j] * sc);
-      *(bf16x8*)((bf16*)out + ((size_t)r * H + h) * d_c + d) = o8;
+    for (int j = 0; j < NP; ++j) {
+      const int i = p0 + j < n ? p0 + j : n - 1;
+      const int slot = i == 0 ? s0 : 2 * (w0 + i);
+      l[j] = p0 + j < n ? pl.part_lse[(size_t)slot * H + h] : -INFINITY;
+      v[j] = *(const vec_t*)((const OutT*)pl.part_o + ((size_t)slot * H + h) * d_c + d);
     }
-  } else if ((d_c & 3) == 0) {
-    const int q4 = d_c >> 2;
-    for (int idx = threadIdx.x; idx < nh * q4; idx += blockDim.x) {
-      const int hh = idx / q4, d = (idx - hh * q4) * 4;
-      const int h = h0 + hh;
-      f32x4 acc = f32x4{};
-      for (int i = 0; i < n; ++i) {
-        const int slot = plan_slot(w0 + i, c0, per);
-        const f32x4 v = load4_f32((const OutT*)pl.part_o + ((size_t)slot * H + h) * d_c + d);
-        acc += w_s[hh][i] * v;
-      }
-      OutT* o = out + ((size_t)r * H + h) * d_c + d;
-      const float sc = inv_s[hh];
-      store_f32(o + 0, acc[0] * sc);
-      store_f32(o + 1, acc[1] * sc);
-      store_f32(o + 2, acc[2] * sc);
-      store_f32(o + 3, acc[3] * sc);
+    float m2 = mx;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) m2 = fmaxf(m2, l[j]);
+    if (m2 == -INFINITY) continue;  // every part so far empty
+    const float sc = __expf(mx - m2);
+    ws *= sc;
+#pragma unroll
+    for (int x = 0; x < VEC; ++x) acc[x] *= sc;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const float w = __expf(l[j] - m2);
+      ws += w;
+#pragma unroll
+      for (int x = 0; x < VEC; ++x) acc[x] += w * (float)v[j][x];
     }
-  } else {
-    for (int idx = threadIdx.x; idx < nh * d_c; idx += blockDim.x) {
-      const int hh = idx / d_c, d = idx - hh * d_c;
-      const int h = h0 + hh;
-      float acc = 0.f;
-      for (int i = 0; i < n; ++i)
-        acc += w_s[hh][i] * load_f32((const OutT*)pl.part_o + ((size_t)plan_slot(w0 + i, c0, per) * H + h) * d_c + d);
-      store_f32(out + ((size_t)r * H + h) * d_c + d, acc * inv_s[hh]);
-    }
+    mx = m2;
   }
+  if (flagged) return;
+  const float inv = ws > 0.f ? 1.0f / ws : 0.f;
+  vec_t o;
+#pragma unroll
+  for (int x = 0; x < VEC; ++x) {
+    if constexpr (sizeof(OutT) == 2)
+      o[x] = f32_to_bf16(acc[x] * inv);
+    else
+      o[x] = acc[x] * inv;
+  }
+  *(vec_t*)(out + ((size_t)r * H + h) * d_c + d) = o;
+  if (lse && d == 0) lse[(size_t)r * H + h] = ws > 0.f ? mx + __logf(ws) : -INFINITY;
 }
 
 template <typename OutT>
@@ -1089,9 +1064,21 @@ static int launch_attention_t(const AttnCall& c) {
   }
   MLA_LAUNCH_CHECK();
   if (c.timing_events && hipEventRecord((hipEvent_t)c.timing_events[1], c.stream) != hipSuccess) return MLA_ERR_HIP;
-  dim3 cgrid(c.G, (c.H + CHB - 1) / CHB);
-  hipLaunchKernelGGL(plan_combine_kernel<T>, cgrid, dim3(256), 0, c.stream, pl, c.H, c.d_c, (T*)c.out, c.lse);
-  MLA_LAUNCH_CHECK();
+  {
+    // at most min(R, G - 1) rows are cut by the G - 1 worker boundaries
+    const unsigned max_split = (unsigned)(c.R < c.G ? c.R : c.G);
+    constexpr int VEC = 16 / (int)sizeof(T);
+    if (c.d_c % VEC == 0 && aligned16(c.out)) {
+      dim3 cgrid((unsigned)((c.H * (c.d_c / VEC) + 255) / 256), max_split);
+      hipLaunchKernelGGL((plan_combine_kernel<T, VEC>), cgrid, dim3(256), 0, c.stream, pl, c.H, c.d_c, (T*)c.out,
+                         c.lse);
+    } else {
+      dim3 cgrid((unsigned)((c.H * c.d_c + 255) / 256), max_split);
+      hipLaunchKernelGGL((plan_combine_kernel<T, 1>), cgrid, dim3(256), 0, c.stream, pl, c.H, c.d_c, (T*)c.out,
+                         c.lse);
+    }
+    MLA_LAUNCH_CHECK();
+  }
   return MLA_OK;
 }
 

@@ -62,7 +62,8 @@ struct Plan {
   int32_t* cum;     // [R + 1]: exclusive prefix sum of tiles per row (cum[R] = total)
   int32_t* len;     // [R]: visible positions per row (clamped)
   int32_t* flags;   // [R]: set when a row had to be recomputed (see the attention kernel)
-  int32_t* split;   // [1 + G]: count, then the rows cut by a worker boundary
+  int32_t* split;   // [4 + 4G]: count, then per row cut by a worker boundary {row, slot of its first part,
+                    //   its first worker, number of parts} (16-byte entries from index 4)
   int32_t* wrow;    // [G]: first row of every worker that has tiles
   float* part_o;    // [2G, H, d_c] partial outputs, stored in the call's dtype (bf16 calls use half the region)
   float* part_lse;  // [2G, H]
@@ -77,7 +78,7 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size
 inline size_t plan_bytes(int64_t R, int G, int H, int d_c) {
   size_t b = align256(sizeof(int32_t) * (size_t)(R + 1));
   b += 2 * align256(sizeof(int32_t) * (size_t)R);
-  b += align256(sizeof(int32_t) * (size_t)(G + 1));
+  b += align256(sizeof(int32_t) * (size_t)(4 + 4 * G));
   b += align256(sizeof(int32_t) * (size_t)G);
   b += align256(sizeof(float) * (size_t)2 * G * H * d_c);
   b += align256(sizeof(float) * (size_t)2 * G * H);
@@ -94,7 +95,7 @@ inline Plan plan_layout(void* ws, int R, int G, int H, int d_c, int tile) {
   pl.flags = (int32_t*)p;
   p += align256(sizeof(int32_t) * (size_t)R);
   pl.split = (int32_t*)p;
-  p += align256(sizeof(int32_t) * (size_t)(G + 1));
+  p += align256(sizeof(int32_t) * (size_t)(4 + 4 * G));
   pl.wrow = (int32_t*)p;
   p += align256(sizeof(int32_t) * (size_t)G);
   pl.part_o = (float*)p;
