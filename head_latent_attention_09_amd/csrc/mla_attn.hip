@@ -281,12 +281,13 @@ constexpr int NBUF = 4;                      // tile buffers in LDS
 constexpr int AHEAD = NBUF - 1;              // tiles issued ahead of the tile whose values are read
 constexpr int KS = WD / 32;                  // k-steps of 32 dims in the score contraction (18)
 constexpr int KL = DC / 32;                  // k-steps over the latent dims (16); the rest are rope dims
-constexpr int KQ = 12;                       // k-steps whose query operand stays in registers
+constexpr int KQ = 14;                       // k-steps whose query operand stays in registers
 constexpr int NW = 4;                        // waves per workgroup
 constexpr int QR_ROW = (WD - 32 * KQ) * 2 + 16;     // query rest: bytes per head row (16 B of padding)
-constexpr int QR_BYTES = 13 * 1024;                 // per wave: 32 rows of QR_ROW bytes, in whole 1 KiB loads
+constexpr int QR_BYTES = 9 * 1024;                  // per wave: 32 rows of QR_ROW bytes, in whole 1 KiB loads
+static_assert(32 * QR_ROW <= QR_BYTES, "query block in LDS");
 constexpr int P_BYTES = 32 * NW * TILE * 2;  // bf16 softmax weights of one tile, 128 heads (4 KiB)
-constexpr int RING = 6;                      // score operand (tile) reads in flight per wave
+constexpr int RING = 5;                      // score operand (tile) reads in flight per wave
 constexpr int QA = 2;                        // k-steps the query operand reads from LDS run ahead
 constexpr int DW = DC / NW;                  // output dims per wave in the value product
 constexpr float SLACK = 64.0f;               // log2 units a score may exceed the reference max
@@ -341,15 +342,33 @@ struct Args {
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 // Score MFMAs with the accumulator pinned to VGPRs (the AGPRs hold the output
-// accumulator). Invisible to the compiler's hazard checker: a VALU read of
-// the result must be at least 11 wait states after the MFMA (see sync_scores).
+// accumulator). Invisible to the compiler's hazard checker, so the code covers
+// both sides itself. Before the MFMA: an operand written by a VALU
+// instruction needs two wait states; GUARD adds them, for kernels whose free
+// AGPRs the compiler uses to park query registers (fewer than 128 heads: it
+// copies them back right before the MFMA). With 128 heads every AGPR holds the
+// output and no such copy is made; a CPU test scans the generated code of
+// every instantiation for a VALU write of an operand within two wait states
+// of an unguarded MFMA. After the chain: sync_scores, which the accumulators
+// pass through, so that no read of the result is placed before the wait
+// states it needs.
+template <bool GUARD>
 __device__ __forceinline__ void mfma16(f32x4& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  if (GUARD)
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
+template <bool GUARD>
 __device__ __forceinline__ void mfma16_first(f32x4& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  if (GUARD)
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void sync_scores() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
+__device__ __forceinline__ void sync_scores(f32x4& a, f32x4& b) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(a), "+v"(b)::"memory");
+}
 
 // Direct global->LDS load of 64 lanes x 16 bytes: lane l reads 16 bytes at
 // gbase + voff and writes them to LDS address lds + 16 l. Issued from inline
@@ -636,11 +655,11 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
       const bf16x8 a_op = kr[ks % RING];
       __builtin_amdgcn_sched_barrier(0);
       if (ks == 0) {
-        mfma16_first(acc[0], a_op, b0);
-        mfma16_first(acc[1], a_op, b1);
+        mfma16_first<(NHB < 4)>(acc[0], a_op, b0);
+        mfma16_first<(NHB < 4)>(acc[1], a_op, b1);
       } else {
-        mfma16(acc[0], a_op, b0);
-        mfma16(acc[1], a_op, b1);
+        mfma16<(NHB < 4)>(acc[0], a_op, b0);
+        mfma16<(NHB < 4)>(acc[1], a_op, b1);
       }
       if (ks + RING < KS) kr[ks % RING] = kread(boff, ks + RING);
       if (ks + QA >= KQ && ks + QA < KS) {
@@ -655,7 +674,7 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
   // first tile's scores and the segment's reference max
   kprefetch(0);
   scores(0, s0, [](int) {});
-  sync_scores();
+  sync_scores(s0[0], s0[1]);
   {
     const int nvalid = len - lt0 * TILE;
 #pragma unroll
@@ -721,7 +740,7 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
           if ((ks & 3) == 1) soft2(ks >> 2);
           if (pre && (ks & 3) == 0) load_tile(ns, nboff, ks >> 2);
         });
-        sync_scores();
+        sync_scores(sn[0], sn[1]);
       } else {
 #pragma unroll
         for (int pi = 0; pi < 4; ++pi) soft2(pi);
