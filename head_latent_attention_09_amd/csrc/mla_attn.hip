@@ -35,20 +35,37 @@ __device__ __forceinline__ int row_len(const RowMap& m, int r) {
 template <typename OutT>
 __global__ __launch_bounds__(1024) void plan_kernel(RowMap m, Plan pl, int H, int d_c, OutT* out, float* lse) {
   __shared__ int sums[1024];
-  __shared__ int nsplit;
+  __shared__ int nsplit, all_tiles, all_rows;
   const int tid = threadIdx.x;
   const int R = pl.R, tile = pl.tile;
   const int chunk = (R + 1023) / 1024;
   const int r0 = min(tid * chunk, R), r1 = min(r0 + chunk, R);
-  if (tid == 0) nsplit = 0;
-  int s = 0;
+  if (tid == 0) nsplit = all_tiles = all_rows = 0;
+  __syncthreads();
+  int nt = 0, nr = 0;
   for (int r = r0; r < r1; ++r) {
     int n = row_len(m, r);
     pl.len[r] = n;
     pl.flags[r] = 0;
-    s += (n + tile - 1) / tile;
+    nt += (n + tile - 1) / tile;
+    nr += n > 0;
   }
-  sums[tid] = s;
+  int wt = nt, wr = nr;  // wave sums, then one shared atomic per wave
+  for (int o = 32; o > 0; o >>= 1) {
+    wt += __shfl_xor(wt, o);
+    wr += __shfl_xor(wr, o);
+  }
+  if ((tid & 63) == 0) {
+    atomicAdd(&all_tiles, wt);
+    atomicAdd(&all_rows, wr);
+  }
+  __syncthreads();
+  // fixed cost per row only when rows are shorter on average than a worker's
+  // share of the tiles (many rows per worker); longer rows are cut into about
+  // equal pieces anyway, and every piece pays the fixed cost
+  const int seg_cost = all_rows > 0 && all_tiles / all_rows < plan_per_worker(all_tiles, pl.G) ? SEG_COST : 0;
+  if (tid == 0) pl.split[1] = seg_cost;
+  sums[tid] = nt + seg_cost * nr;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan
     int v = tid >= off ? sums[tid - off] : 0;
@@ -60,14 +77,15 @@ __global__ __launch_bounds__(1024) void plan_kernel(RowMap m, Plan pl, int H, in
   const int per = plan_per_worker(total, pl.G);
   int base = tid == 0 ? 0 : sums[tid - 1];
   for (int r = r0; r < r1; ++r) {
-    const int n = (pl.len[r] + tile - 1) / tile;
+    const int n = row_units((pl.len[r] + tile - 1) / tile, seg_cost);
     pl.cum[r] = base;
-    if (n > 0 && base / per != (base + n - 1) / per) {
-      const int w0 = base / per;
+    const int s0 = base + seg_cost;  // first unit of the row's tiles
+    if (n > 0 && s0 / per != (base + n - 1) / per) {
+      const int w0 = s0 / per;
       *(int4*)(pl.split + 4 + 4 * atomicAdd(&nsplit, 1)) =
-          int4{r, plan_slot(w0, base, per), w0, (base + n - 1) / per - w0 + 1};
+          int4{r, plan_slot(w0, s0, per), w0, (base + n - 1) / per - w0 + 1};
     }
-    // workers whose range starts inside this row's tiles begin with this row
+    // workers whose range starts inside this row's units begin with this row
     for (int w = (base + per - 1) / per; n > 0 && w * per < base + n && w < pl.G; ++w) pl.wrow[w] = r;
     base += n;
   }
@@ -253,6 +271,7 @@ __global__ __launch_bounds__(NT) void attn_generic_kernel(Args<T> a) {
   const int w = xcd_worker(blockIdx.x, G);
   const int h0 = blockIdx.y * HG;
   const int total = a.pl.cum[a.pl.R];
+  const int seg_cost = a.pl.split[1];
   const int per = plan_per_worker(total, G);
   const int t_begin = w * per;
   if (t_begin >= total) return;
@@ -260,11 +279,9 @@ __global__ __launch_bounds__(NT) void attn_generic_kernel(Args<T> a) {
   for (int r = a.pl.wrow[w]; r < a.pl.R; ++r) {
     const int c0 = a.pl.cum[r], c1 = a.pl.cum[r + 1];
     if (c0 >= t_end) break;
-    if (c1 <= t_begin || c1 == c0) continue;
-    const int lt0 = max(t_begin, c0) - c0, lt1 = min(t_end, c1) - c0;
-    const bool full = c0 >= t_begin && c1 <= t_end;
-    attend_segment<T>(a, r, lt0, lt1, full, plan_slot(w, c0, per), h0, tile, qs, ps, alpha_s, stat_s,
-                      m_run, l_run);
+    Segment sg;
+    if (!plan_segment(c0, c1, seg_cost, t_begin, t_end, w, per, sg)) continue;
+    attend_segment<T>(a, r, sg.lt0, sg.lt1, sg.full, sg.slot, h0, tile, qs, ps, alpha_s, stat_s, m_run, l_run);
   }
 }
 }  // namespace gn
@@ -888,6 +905,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(Args a) {
   const int G = a.pl.G;
   const int w = xcd_worker(blockIdx.x, G);
   const int total = a.pl.cum[a.pl.R];
+  const int seg_cost = a.pl.split[1];
   const int per = plan_per_worker(total, G);
   const int t_begin = w * per;
   if (t_begin >= total) return;
@@ -895,10 +913,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(Args a) {
   for (int r = a.pl.wrow[w]; r < a.pl.R; ++r) {
     const int c0 = a.pl.cum[r], c1 = a.pl.cum[r + 1];
     if (c0 >= t_end) break;
-    if (c1 <= t_begin || c1 == c0) continue;
-    const int lt0 = max(t_begin, c0) - c0, lt1 = min(t_end, c1) - c0;
-    const bool full = c0 >= t_begin && c1 <= t_end;
-    attend_segment<NHB>(a, r, lt0, lt1, full, plan_slot(w, c0, per), smem, &seg_flag, lane, wv);
+    Segment sg;
+    if (!plan_segment(c0, c1, seg_cost, t_begin, t_end, w, per, sg)) continue;
+    attend_segment<NHB>(a, r, sg.lt0, sg.lt1, sg.full, sg.slot, smem, &seg_flag, lane, wv);
   }
 }
 }  // namespace mf

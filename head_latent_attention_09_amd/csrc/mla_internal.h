@@ -48,22 +48,33 @@ template <> __device__ __forceinline__ void store_f32<bf16>(bf16* p, float v) { 
 //
 // The work of a call is a list of R "rows" (decode: one per sequence;
 // prefill: one per query), each with len[r] visible positions cut into
-// tiles of TILE positions. Tiles of all rows are concatenated in row order
-// and dealt out in equal contiguous ranges of `per_worker` tiles to G
-// workers (one workgroup each). A worker's range is a run of segments, one
-// per row it touches. A row entirely inside one worker is finished by that
-// worker; a row cut by worker boundaries leaves one partial result
-// (normalised output in the call's dtype + fp32 lse) per touching worker,
-// merged by the combine.
-// Partial slot of (worker w, row r): 2w if r started before w's range
-// (r is w's first segment), else 2w + 1 (r runs past w's end). So 2G slots.
+// tiles of TILE positions. Work is measured in units: one per tile, plus a
+// fixed cost c for every row that has tiles (a segment's fixed work: query
+// load, pipeline fill, normalisation and output write). Rows are laid out in
+// row order on the unit axis, a non-empty row as c units of fixed cost
+// followed by one unit per tile, and the axis is dealt out in equal
+// contiguous ranges of `per_worker` units to G workers (one workgroup
+// each). c is SEG_COST when rows are on average shorter than a worker's
+// share of tiles: without it, workers given many short rows (the first
+// queries of a causal prefill) would take several times longer than the
+// rest. Otherwise c is 0: long rows are cut into pieces that each pay the
+// fixed cost, which equal tile ranges already balance. The plan stores c in
+// split[1]. A worker's range is a run of segments, one per row with tiles in
+// it. A row whose tiles all fall in one worker is finished there; a row
+// whose tiles are cut by worker boundaries leaves one partial result
+// (normalised output in the call's dtype + fp32 lse) per worker holding
+// some of its tiles, merged by the combine.
+// Partial slot of (worker w, row r): 2w if r's tiles started before w's
+// range (r is w's first segment), else 2w + 1 (r runs past w's end). So 2G
+// slots.
 // ---------------------------------------------------------------------------
 struct Plan {
-  int32_t* cum;     // [R + 1]: exclusive prefix sum of tiles per row (cum[R] = total)
+  int32_t* cum;     // [R + 1]: exclusive prefix sum of units per row (cum[R] = total)
   int32_t* len;     // [R]: visible positions per row (clamped)
   int32_t* flags;   // [R]: set when a row had to be recomputed (see the attention kernel)
-  int32_t* split;   // [4 + 4G]: count, then per row cut by a worker boundary {row, slot of its first part,
-                    //   its first worker, number of parts} (16-byte entries from index 4)
+  int32_t* split;   // [4 + 4G]: count, the fixed cost per row c, then per row cut by a worker boundary
+                    //   {row, slot of its first part, its first worker, number of parts} (16-byte entries
+                    //   from index 4)
   int32_t* wrow;    // [G]: first row of every worker that has tiles
   float* part_o;    // [2G, H, d_c] partial outputs, stored in the call's dtype (bf16 calls use half the region)
   float* part_lse;  // [2G, H]
@@ -107,6 +118,11 @@ inline Plan plan_layout(void* ws, int R, int G, int H, int d_c, int tile) {
   return pl;
 }
 
+constexpr int SEG_COST = 12;  // fixed work of a segment, in tile units (measured: about 12 tiles' time)
+
+// units of a row with n tiles under a fixed cost c per row
+__host__ __device__ inline int row_units(int n, int c) { return n > 0 ? n + c : 0; }
+
 __device__ __forceinline__ int plan_per_worker(int total, int G) {
   int q = (total + G - 1) / G;
   return q < 1 ? 1 : q;
@@ -120,8 +136,27 @@ __device__ __forceinline__ int xcd_worker(int bx, int G) {
   return (bx % 8) * (G / 8) + bx / 8;
 }
 
-__device__ __forceinline__ int plan_slot(int w, int row_start_tile, int per_worker) {
-  return (row_start_tile < w * per_worker) ? 2 * w : 2 * w + 1;
+__device__ __forceinline__ int plan_slot(int w, int row_tile_start, int per_worker) {
+  return (row_tile_start < w * per_worker) ? 2 * w : 2 * w + 1;
+}
+
+// The segment of row r (units [c0, c1), fixed cost `cost`) in a worker's unit range [t_begin,
+// t_end): tiles [lt0, lt1) of the row, whether they are all of its tiles,
+// and the partial slot. False when the worker holds none of its tiles.
+struct Segment {
+  int lt0, lt1, slot;
+  bool full;
+};
+__device__ __forceinline__ bool plan_segment(int c0, int c1, int cost, int t_begin, int t_end, int w, int per,
+                                             Segment& sg) {
+  if (c1 == c0) return false;
+  const int s0 = c0 + cost;
+  if (c1 <= t_begin || s0 >= t_end) return false;
+  sg.lt0 = max(t_begin, s0) - s0;
+  sg.lt1 = min(t_end, c1) - s0;
+  sg.full = s0 >= t_begin && c1 <= t_end;
+  sg.slot = plan_slot(w, s0, per);
+  return true;
 }
 
 // description of where row r's query, cache and output live
