@@ -201,7 +201,7 @@ def main():
                    "cache": "dense", "workers": G_workers, "rotated_copies": args.copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "latent attention (mla::mf::attn_mfma_kernel<4>)",
+                     "kernel": "latent attention (mla::mf::attn_mfma_kernel<4, true>)",
                      "avg_launch_ms": round(attn_avg, 5), "alg_bytes_per_launch": alg_bytes},
         "roofline_mfma": {"achieved": round(alg_flop / (attn_avg / 1e3) / 1e12, 1), "peak": BF16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(alg_flop / (attn_avg / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),

@@ -399,12 +399,18 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(gbase), "s"(lds) : "memory");
 }
-// The same for data read once (cache tiles): non-temporal, so the stream does
-// not displace reused lines; measured 1.27x the streaming rate of the
-// default policy for this load pattern.
-__device__ __forceinline__ void dma16_stream(const void* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-               :: "v"(voff), "s"(gbase), "s"(lds) : "memory");
+// Cache tile loads. Decode reads each cache row once: non-temporal, so the
+// stream does not displace reused lines (measured 1.27x the streaming rate
+// of the default policy for this load pattern). A causal prefill reads the
+// same rows for every query of the sequence: default policy, so they stay
+// in L2 (measured 7 % faster there).
+template <bool STREAM>
+__device__ __forceinline__ void dma16_tile(const void* gbase, uint32_t voff, uint32_t lds) {
+  if (STREAM)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(voff), "s"(gbase), "s"(lds) : "memory");
+  else
+    dma16(gbase, voff, lds);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -484,22 +490,24 @@ __device__ __forceinline__ TileSrc tile_src(const Args& a, int b, int t0, int le
 // lane ^ sC(wv): sC(wv + 4k) = sC(wv) ^ k.
 __device__ __forceinline__ int loads_per_tile(int wv) { return wv < 2 ? 5 : 4; }
 
+template <bool STREAM>
 __device__ __forceinline__ void issue_load(const TileSrc& s, char* buf, int k, int lx, int lane, int wv) {
   if (k < 4) {
     const int ld = wv + NW * k;
     const int row = ld < s.last ? ld : s.last;
-    dma16_stream(s.p + (size_t)row * (WD * 2), (uint32_t)((lx ^ k) << 4), lds_addr(buf + ld * 1024));
+    dma16_tile<STREAM>(s.p + (size_t)row * (WD * 2), (uint32_t)((lx ^ k) << 4), lds_addr(buf + ld * 1024));
   } else if (wv < 2) {
     const int rl = 8 * wv + (lane >> 3);
     const int row = rl < s.last ? rl : s.last;
-    dma16_stream(s.p, (uint32_t)(row * (WD * 2) + DC * 2 + (((lane & 7) ^ sR(rl)) << 4)),
+    dma16_tile<STREAM>(s.p, (uint32_t)(row * (WD * 2) + DC * 2 + (((lane & 7) ^ sR(rl)) << 4)),
                  lds_addr(buf + C_BYTES + wv * 1024));
   }
 }
 
+template <bool STREAM>
 __device__ __forceinline__ void issue_tile(const TileSrc& s, char* buf, int lx, int lane, int wv) {
 #pragma unroll
-  for (int k = 0; k < 5; ++k) issue_load(s, buf, k, lx, lane, wv);
+  for (int k = 0; k < 5; ++k) issue_load<STREAM>(s, buf, k, lx, lane, wv);
 }
 
 
@@ -530,7 +538,7 @@ __device__ void recompute_row(const Args& a, int r, char* smem) {
   __syncthreads();
 }
 
-template <int NHB>
+template <int NHB, bool STREAM>
 __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, int lt1, bool full, int slot,
                                                char* smem, int* seg_flag, int lane, int wv) {
   constexpr int H = 32 * NHB;
@@ -560,7 +568,7 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
     opaque(ln);
     const int lx = ln ^ sC(wv);
     const int np = ntiles < AHEAD ? ntiles : AHEAD;
-    for (int j = 0; j < (np < 2 ? np : 2); ++j) issue_tile(tile_src(a, b, (lt0 + j) * TILE, len), tbuf(j), lx, ln, wv);
+    for (int j = 0; j < (np < 2 ? np : 2); ++j) issue_tile<STREAM>(tile_src(a, b, (lt0 + j) * TILE, len), tbuf(j), lx, ln, wv);
     {
       const char* qbase = (const char*)(a.q + ((size_t)r * H + wq * 32) * WD + 32 * KQ);
       constexpr int QC = QR_ROW / 16;  // 16-byte slots per row, the last one padding
@@ -572,7 +580,7 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
         dma16(qbase, (uint32_t)(hr * (WD * 2) + (pc << 4)), lds_addr(qr_lds + k * 1024));
       }
     }
-    for (int j = 2; j < np; ++j) issue_tile(tile_src(a, b, (lt0 + j) * TILE, len), tbuf(j), lx, ln, wv);
+    for (int j = 2; j < np; ++j) issue_tile<STREAM>(tile_src(a, b, (lt0 + j) * TILE, len), tbuf(j), lx, ln, wv);
     {
       const bf16* qrow = a.q + ((size_t)r * H + wq * 32 + (ln & 15)) * WD + (ln >> 4) * 8;
 #pragma unroll
@@ -634,10 +642,10 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
     if (k < 4) {
       const int ld = wv + NW * k;
       const int row = ld < s.last ? ld : s.last;
-      dma16_stream(s.p + (size_t)row * (WD * 2), (uint32_t)(dofs ^ (k << 4)), lds_addr(buf + ld * 1024));
+      dma16_tile<STREAM>(s.p + (size_t)row * (WD * 2), (uint32_t)(dofs ^ (k << 4)), lds_addr(buf + ld * 1024));
     } else if (wv < 2) {
       const int row = s.last >= TILE - 1 ? rrow : (rrow < s.last ? rrow : s.last);
-      dma16_stream(s.p, (uint32_t)(row * (WD * 2) + rdofs), lds_addr(buf + C_BYTES + wv * 1024));
+      dma16_tile<STREAM>(s.p, (uint32_t)(row * (WD * 2) + rdofs), lds_addr(buf + C_BYTES + wv * 1024));
     }
   };
 
@@ -896,7 +904,7 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
   }
 }
 
-template <int NHB>
+template <int NHB, bool STREAM>
 __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(Args a) {
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   __shared__ int seg_flag;
@@ -915,7 +923,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(Args a) {
     if (c0 >= t_end) break;
     Segment sg;
     if (!plan_segment(c0, c1, seg_cost, t_begin, t_end, w, per, sg)) continue;
-    attend_segment<NHB>(a, r, sg.lt0, sg.lt1, sg.full, sg.slot, smem, &seg_flag, lane, wv);
+    attend_segment<NHB, STREAM>(a, r, sg.lt0, sg.lt1, sg.full, sg.slot, smem, &seg_flag, lane, wv);
   }
 }
 }  // namespace mf
@@ -1089,11 +1097,21 @@ static int launch_attention_t(const AttnCall& c) {
     a.scale_log2 = c.kq_scale * kLog2e;
     a.out = (bf16*)c.out;
     a.lse = c.lse;
-    switch (c.H / 32) {
-      case 1: hipLaunchKernelGGL(mf::attn_mfma_kernel<1>, dim3(c.G), dim3(mf::NW * 64), 0, c.stream, a); break;
-      case 2: hipLaunchKernelGGL(mf::attn_mfma_kernel<2>, dim3(c.G), dim3(mf::NW * 64), 0, c.stream, a); break;
-      case 3: hipLaunchKernelGGL(mf::attn_mfma_kernel<3>, dim3(c.G), dim3(mf::NW * 64), 0, c.stream, a); break;
-      default: hipLaunchKernelGGL(mf::attn_mfma_kernel<4>, dim3(c.G), dim3(mf::NW * 64), 0, c.stream, a); break;
+    const dim3 grid(c.G), block(mf::NW * 64);
+    if (c.map.mode != 2) {  // decode: every cache row read once
+      switch (c.H / 32) {
+        case 1: hipLaunchKernelGGL((mf::attn_mfma_kernel<1, true>), grid, block, 0, c.stream, a); break;
+        case 2: hipLaunchKernelGGL((mf::attn_mfma_kernel<2, true>), grid, block, 0, c.stream, a); break;
+        case 3: hipLaunchKernelGGL((mf::attn_mfma_kernel<3, true>), grid, block, 0, c.stream, a); break;
+        default: hipLaunchKernelGGL((mf::attn_mfma_kernel<4, true>), grid, block, 0, c.stream, a); break;
+      }
+    } else {  // causal prefill: rows re-read by every later query
+      switch (c.H / 32) {
+        case 1: hipLaunchKernelGGL((mf::attn_mfma_kernel<1, false>), grid, block, 0, c.stream, a); break;
+        case 2: hipLaunchKernelGGL((mf::attn_mfma_kernel<2, false>), grid, block, 0, c.stream, a); break;
+        case 3: hipLaunchKernelGGL((mf::attn_mfma_kernel<3, false>), grid, block, 0, c.stream, a); break;
+        default: hipLaunchKernelGGL((mf::attn_mfma_kernel<4, false>), grid, block, 0, c.stream, a); break;
+      }
     }
   } else {
     launch_generic<T>(c, pl);
