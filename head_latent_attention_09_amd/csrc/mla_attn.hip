@@ -869,26 +869,23 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
       }
     }
   }
+  // The output is staged through LDS (the tile ring is free now) so that
+  // every global store writes whole 1 KiB rows: the accumulator layout holds
+  // 4 dims of 32 heads per store, which would write partial cache lines.
+  // Head blocks are staged two at a time (64 rows of OROW bytes).
   const int g = le >> 5;
+  bf16* const dst = full ? a.out + (size_t)r * H * DC : (bf16*)a.pl.part_o + (size_t)slot * H * DC;
+  constexpr int OROW = DC * 2 + 16;  // 16 bytes of padding spread a column's rows over the banks
+  static_assert(64 * OROW <= NBUF * TILE_BYTES, "output staging fits the tile ring");
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) {
-    const int hh = 32 * hb + (le & 31);
-    const float inv = inv_s[hh];
-    if (full) {
-      bf16* orow = a.out + ((size_t)r * H + hh) * DC + DW * wv;
+  for (int half = 0; half < (NHB + 1) / 2; ++half) {
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          bf16x4 v;
-          v[0] = f32_to_bf16(o[hb][d][4 * rq + 0] * inv);
-          v[1] = f32_to_bf16(o[hb][d][4 * rq + 1] * inv);
-          v[2] = f32_to_bf16(o[hb][d][4 * rq + 2] * inv);
-          v[3] = f32_to_bf16(o[hb][d][4 * rq + 3] * inv);
-          *(bf16x4*)(orow + d * 32 + 8 * rq + 4 * g) = v;
-        }
-    } else {
-      bf16* prow = (bf16*)a.pl.part_o + ((size_t)slot * H + hh) * DC + DW * wv;
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int hb = 2 * half + h2;
+      if (hb >= NHB) break;
+      const int hh = 32 * hb + (le & 31);
+      const float inv = inv_s[hh];
+      char* lrow = smem + (32 * h2 + (le & 31)) * OROW + 2 * DW * wv;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -898,9 +895,14 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
           v[1] = f32_to_bf16(o[hb][d][4 * rq + 1] * inv);
           v[2] = f32_to_bf16(o[hb][d][4 * rq + 2] * inv);
           v[3] = f32_to_bf16(o[hb][d][4 * rq + 3] * inv);
-          *(bf16x4*)(prow + d * 32 + 8 * rq + 4 * g) = v;
+          *(MLA_LDS bf16x4*)(lrow + 2 * (d * 32 + 8 * rq + 4 * g)) = v;
         }
     }
+    __syncthreads();
+    const int nrows = H - 64 * half < 64 ? H - 64 * half : 64;
+    for (int i = wv; i < nrows; i += NW)
+      *(bf16x8*)(dst + (size_t)(64 * half + i) * DC + 8 * le) = *(const MLA_LDS bf16x8*)(smem + i * OROW + 16 * le);
+    __syncthreads();  // the staging rows are read before the next half overwrites them
   }
 }
 
