@@ -75,7 +75,7 @@ def check_decode(case, num_workers=0, label=""):
 
 
 @pytest.mark.parametrize("dtype", [G.BF16, G.F32])
-@pytest.mark.parametrize("H", [128, 64, 16])
+@pytest.mark.parametrize("H", [128, 96, 64, 32, 16])
 def test_decode_dense_small(dtype, H):
     lens = [1, 45, 100, 0, 257]
     case = G.decode_case(5, H, 512, 64, lens, dtype, seed=100 + H, cache_rows=300)
@@ -88,6 +88,15 @@ def test_decode_split_count_invariance(workers):
     case = G.decode_case(3, 128, 512, 64, [700, 33, 1000], G.BF16, seed=7)
     case.kq_scale = 1.0 / math.sqrt(192)
     check_decode(case, num_workers=workers, label="split invariance")
+
+
+@pytest.mark.parametrize("workers", [200, 0])
+def test_decode_row_over_many_workers(workers):
+    """One long row cut into one or two tiles per worker: the combine merges
+    about 190 partial results per row (its multi-pass path)."""
+    case = G.decode_case(1, 128, 512, 64, [3000], G.BF16, seed=41)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    check_decode(case, num_workers=workers, label="many parts")
 
 
 @pytest.mark.parametrize("dtype", [G.BF16, G.F32])
@@ -236,6 +245,28 @@ def test_prefill_chain_small(dtype, H, d_c, d_r, d_nope, d_v, S_q, S_kv):
             ev = max(ev, rel_err(gv[b, i], rv))
         say(f"  b={b}: out {e:.2e} lse {le:.2e} v(unabsorbed) {ev:.2e}")
         assert e <= tol and le <= LSE_TOL[dtype] and ev <= tol
+
+
+@pytest.mark.parametrize("workers", [1, 4, 64, 0])
+def test_prefill_split_count_invariance(workers):
+    """Causal prefill with many short rows per worker (the plan charges each
+    row a fixed cost) and rows cut across workers, at several worker counts."""
+    say(f"prefill split invariance: workers={workers}")
+    case = G.prefill_case(2, 160, 160, 32, 128, 512, 64, 128, G.BF16, seed=23)
+    rng = np.random.default_rng(23)   # absorbed queries drawn directly: [q_abs ~ N(0, 1/512) | q_pe ~ N(0, 1)]
+    qa = np.concatenate([rng.standard_normal((2, 160, 32, 512)) / math.sqrt(512),
+                         rng.standard_normal((2, 160, 32, 64))], axis=-1)
+    q = to_dev(G.storage(qa, G.BF16), G.BF16)
+    cache = to_dev(case.cache, G.BF16)
+    out, lse = M.latent_prefill_causal(q, cache, 512, case.kq_scale, num_workers=workers)
+    torch.cuda.synchronize()
+    got, glse = to_host64(out), lse.cpu().numpy().astype(np.float64)
+    qh = to_host64(q)
+    for b in range(2):
+        ro, rl = O.latent_prefill_causal(qh[b], G.to_f64(case.cache[b], G.BF16), 512, case.kq_scale)
+        e, le = rel_err(got[b], ro), lse_err(glse[b], rl)
+        say(f"  b={b}: out {e:.2e} lse {le:.2e}")
+        assert e <= TOL[G.BF16] and le <= LSE_TOL[G.BF16]
 
 
 @pytest.mark.slow
