@@ -34,48 +34,66 @@ __device__ __forceinline__ int row_len(const RowMap& m, int r) {
 
 template <typename OutT>
 __global__ __launch_bounds__(1024) void plan_kernel(RowMap m, Plan pl, int H, int d_c, OutT* out, float* lse) {
-  __shared__ int sums[1024];
-  __shared__ int nsplit, all_tiles, all_rows;
-  const int tid = threadIdx.x;
+  __shared__ int wsum_t[16], wsum_r[16], wsum_z[16];
+  __shared__ int nsplit;
+  __shared__ int zrows[256];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int R = pl.R, tile = pl.tile;
   const int chunk = (R + 1023) / 1024;
   const int r0 = min(tid * chunk, R), r1 = min(r0 + chunk, R);
-  if (tid == 0) nsplit = all_tiles = all_rows = 0;
-  __syncthreads();
-  int nt = 0, nr = 0;
+  if (tid == 0) nsplit = 0;
+  int nt = 0, nr = 0, nz0 = 0;  // this thread's tiles, non-empty rows and empty rows
   for (int r = r0; r < r1; ++r) {
     int n = row_len(m, r);
     pl.len[r] = n;
     pl.flags[r] = 0;
     nt += (n + tile - 1) / tile;
     nr += n > 0;
+    nz0 += n == 0;
   }
-  int wt = nt, wr = nr;  // wave sums, then one shared atomic per wave
-  for (int o = 32; o > 0; o >>= 1) {
-    wt += __shfl_xor(wt, o);
-    wr += __shfl_xor(wr, o);
+  // inclusive scans of the three counts over the block: within each wave by shuffles,
+  // then across the 16 wave totals (one barrier)
+  int st = nt, sr = nr, sz = nz0;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int yt = __shfl_up(st, o), yr = __shfl_up(sr, o), yz = __shfl_up(sz, o);
+    if (lane >= o) {
+      st += yt;
+      sr += yr;
+      sz += yz;
+    }
   }
-  if ((tid & 63) == 0) {
-    atomicAdd(&all_tiles, wt);
-    atomicAdd(&all_rows, wr);
+  if (lane == 63) {
+    wsum_t[wid] = st;
+    wsum_r[wid] = sr;
+    wsum_z[wid] = sz;
   }
   __syncthreads();
+  int all_tiles = 0, all_rows = 0, nz = 0;
+  for (int i = 0; i < 16; ++i) {
+    const int t = wsum_t[i], c = wsum_r[i], z = wsum_z[i];
+    if (i < wid) {
+      st += t;
+      sr += c;
+      sz += z;
+    }
+    all_tiles += t;
+    all_rows += c;
+    nz += z;
+  }
+  // list the empty rows (written at the end)
+  for (int r = r0, i = sz - nz0; r < r1; ++r)
+    if (pl.len[r] == 0 && i < 256) zrows[i++] = r;
   // fixed cost per row only when rows are shorter on average than a worker's
   // share of the tiles (many rows per worker); longer rows are cut into about
   // equal pieces anyway, and every piece pays the fixed cost
   const int seg_cost = all_rows > 0 && all_tiles / all_rows < plan_per_worker(all_tiles, pl.G) ? SEG_COST : 0;
-  if (tid == 0) pl.split[1] = seg_cost;
-  sums[tid] = nt + seg_cost * nr;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan
-    int v = tid >= off ? sums[tid - off] : 0;
-    __syncthreads();
-    sums[tid] += v;
-    __syncthreads();
-  }
-  const int total = sums[1023];
+  const int total = all_tiles + seg_cost * all_rows;
   const int per = plan_per_worker(total, pl.G);
-  int base = tid == 0 ? 0 : sums[tid - 1];
+  if (tid == 0) {
+    pl.split[1] = seg_cost;
+    pl.cum[R] = total;
+  }
+  int base = (st - nt) + seg_cost * (sr - nr);  // first unit of this thread's rows
   for (int r = r0; r < r1; ++r) {
     const int n = row_units((pl.len[r] + tile - 1) / tile, seg_cost);
     pl.cum[r] = base;
@@ -89,23 +107,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(RowMap m, Plan pl, int H, in
     for (int w = (base + per - 1) / per; n > 0 && w * per < base + n && w < pl.G; ++w) pl.wrow[w] = r;
     base += n;
   }
-  if (tid == 1023) pl.cum[R] = total;
   __syncthreads();
   if (tid == 0) pl.split[0] = nsplit;
   // rows with nothing visible: zeros and lse = -inf (no later kernel touches
-  // them). Each thread checks its own rows; the rare empty rows are written
-  // by the whole workgroup.
-  __shared__ int nzero;
-  __shared__ int zrows[256];
-  if (tid == 0) nzero = 0;
-  __syncthreads();
-  for (int r = r0; r < r1; ++r)
-    if (pl.len[r] == 0) {
-      const int i = atomicAdd(&nzero, 1);
-      if (i < 256) zrows[i] = r;
-    }
-  __syncthreads();
-  const int nz = nzero;
+  // them). The rare empty rows, listed above, are written by the whole
+  // workgroup.
   for (int j = 0; j < (nz < 256 ? nz : 256); ++j) {
     const int r = zrows[j];
     for (int i = tid; i < H * d_c; i += 1024) store_f32(out + (size_t)r * H * d_c + i, 0.f);
