@@ -306,7 +306,7 @@ constexpr int KS = WD / 32;                  // k-steps of 32 dims in the score 
 constexpr int KL = DC / 32;                  // k-steps over the latent dims (16); the rest are rope dims
 constexpr int KQ = 14;                       // k-steps whose query operand stays in registers
 constexpr int NW = 4;                        // waves per workgroup
-constexpr int QR_ROW = (WD - 32 * KQ) * 2 + 16;     // query rest: bytes per head row (16 B of padding)
+constexpr int QR_ROW = (WD - 32 * KQ) * 2 + 32;     // query rest: bytes per head row (32 B of padding)
 constexpr int QR_BYTES = 9 * 1024;                  // per wave: 32 rows of QR_ROW bytes, in whole 1 KiB loads
 static_assert(32 * QR_ROW <= QR_BYTES, "query block in LDS");
 constexpr int P_BYTES = 32 * NW * TILE * 2;  // bf16 softmax weights of one tile, 128 heads (4 KiB)
@@ -337,17 +337,21 @@ constexpr int SMEM_BYTES = LDS_INV + 32 * NW * 4;
 // value fragments are read, and waited for, before the barrier of iteration
 // j - NBUF), and published by the barrier of iteration j - 2.
 //
-// LDS layouts (XOR swizzles keep every read and write pattern below free of
-// bank conflicts on a 256-byte-wide LDS):
+// LDS layouts (XOR swizzles; chosen with the LDS bank-conflict counter on
+// this chip, since its banking is not a plain 4-byte interleave: the score
+// operand reads, the transposing value reads and the query reads below
+// count no conflict):
 //   tile latent row t at t*1024, 16-byte chunk c at c ^ sC(t) inside its
 //     aligned group of 16 chunks; rope row t at C_BYTES + t*128, chunk c at
 //     c ^ sR(t);
-//   query dims 32KQ .. 575: wave block of 32 rows of QR_ROW bytes (the 16
-//     bytes of padding shift consecutive rows across the banks);
+//   query dims 32KQ .. 575: wave block of 32 rows of QR_ROW bytes (32 bytes
+//     of padding per row);
 //   weights: head hh at hh*32 (16 positions), 8-byte quarter q at
 //     q ^ (2 * ((hh >> 3) & 1)).
+// sC is linear in the bits of t (sC(a | b) = sC(a) ^ sC(b) for disjoint a, b)
+// and a permutation of 0..15 over the 16 rows of a tile.
 __device__ __forceinline__ int sC(int r) {
-  return (((r & 1) ? 6 : 0) ^ ((r & 2) ? 10 : 0)) ^ ((r >> 2) & 3);
+  return ((r & 1) ? 4 : 0) ^ ((r & 2) ? 8 : 0) ^ ((r & 4) ? 3 : 0) ^ ((r & 8) ? 6 : 0);
 }
 __device__ __forceinline__ int sR(int r) { return (r ^ (r >> 3)) & 7; }
 
@@ -493,7 +497,7 @@ __device__ __forceinline__ TileSrc tile_src(const Args& a, int b, int t0, int le
 // rows 8wv .. 8wv+7 (one load issue costs the issuing wave about as much as
 // another, so the two rope loads are not split four ways). Rows past the last
 // visible one re-read it (finite data; their weights are zeroed). lx is
-// lane ^ sC(wv): sC(wv + 4k) = sC(wv) ^ k.
+// lane ^ sC(wv): sC(wv + 4k) = sC(wv) ^ sC(4k).
 __device__ __forceinline__ int loads_per_tile(int wv) { return wv < 2 ? 5 : 4; }
 
 template <bool STREAM>
@@ -501,7 +505,7 @@ __device__ __forceinline__ void issue_load(const TileSrc& s, char* buf, int k, i
   if (k < 4) {
     const int ld = wv + NW * k;
     const int row = ld < s.last ? ld : s.last;
-    dma16_tile<STREAM>(s.p + (size_t)row * (WD * 2), (uint32_t)((lx ^ k) << 4), lds_addr(buf + ld * 1024));
+    dma16_tile<STREAM>(s.p + (size_t)row * (WD * 2), (uint32_t)((lx ^ sC(4 * k)) << 4), lds_addr(buf + ld * 1024));
   } else if (wv < 2) {
     const int rl = 8 * wv + (lane >> 3);
     const int row = rl < s.last ? rl : s.last;
@@ -577,12 +581,12 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
     for (int j = 0; j < (np < 2 ? np : 2); ++j) issue_tile<STREAM>(tile_src(a, b, (lt0 + j) * TILE, len), tbuf(j), lx, ln, wv);
     {
       const char* qbase = (const char*)(a.q + ((size_t)r * H + wq * 32) * WD + 32 * KQ);
-      constexpr int QC = QR_ROW / 16;  // 16-byte slots per row, the last one padding
+      constexpr int QC = QR_ROW / 16;  // 16-byte slots per row, the last two padding
 #pragma unroll
       for (int k = 0; k < QR_BYTES / 1024; ++k) {
         const int p = k * 64 + ln;  // 16-byte slot of this wave's block
         int hr = p / QC, pc = p - hr * QC;
-        if (hr > 31 || pc == QC - 1) hr = pc = 0;  // padding and slack: any valid chunk
+        if (hr > 31 || pc >= QC - 2) hr = pc = 0;  // padding and slack: any valid chunk
         dma16(qbase, (uint32_t)(hr * (WD * 2) + (pc << 4)), lds_addr(qr_lds + k * 1024));
       }
     }
@@ -637,7 +641,7 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
   // positions 8(l/32) .. +7 of head 32hb + l%32 (read)
   const int pwo = LDS_P + (wv * 32 + t16) * 32 + ((q4 ^ (2 * ((ln >> 3) & 1))) << 3);
   const int pro = LDS_P + (ln & 31) * 32 + (((ln >> 5) ^ ((ln >> 3) & 1)) << 4);
-  // tile loads: latent load k reads chunk (lane ^ sC(wv) ^ k); the rope load
+  // tile loads: latent load k reads chunk (lane ^ sC(wv) ^ sC(4k)); the rope load
   // (waves 0, 1) reads row 8wv + l/8, chunk (l&7) ^ sR(row)
   const int dofs = (ln ^ sC(wv)) << 4;
   const int rrow = 8 * wv + (ln >> 3);
@@ -648,7 +652,7 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
     if (k < 4) {
       const int ld = wv + NW * k;
       const int row = ld < s.last ? ld : s.last;
-      dma16_tile<STREAM>(s.p + (size_t)row * (WD * 2), (uint32_t)(dofs ^ (k << 4)), lds_addr(buf + ld * 1024));
+      dma16_tile<STREAM>(s.p + (size_t)row * (WD * 2), (uint32_t)(dofs ^ (sC(4 * k) << 4)), lds_addr(buf + ld * 1024));
     } else if (wv < 2) {
       const int row = s.last >= TILE - 1 ? rrow : (rrow < s.last ? rrow : s.last);
       dma16_tile<STREAM>(s.p, (uint32_t)(row * (WD * 2) + rdofs), lds_addr(buf + C_BYTES + wv * 1024));
