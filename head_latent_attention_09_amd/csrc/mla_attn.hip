@@ -301,6 +301,7 @@ constexpr int TILE = 16;                     // positions per tile
 constexpr int C_BYTES = TILE * DC * 2;       // latent rows: 16 x 1024 B
 constexpr int TILE_BYTES = TILE * WD * 2;    // + rope rows: 16 x 128 B = 18 KiB
 constexpr int NBUF = 4;                      // tile buffers in LDS
+static_assert((NBUF & (NBUF - 1)) == 0, "buffer indices are taken with & (NBUF - 1)");
 constexpr int AHEAD = NBUF - 1;              // tiles issued ahead of the tile whose values are read
 constexpr int KS = WD / 32;                  // k-steps of 32 dims in the score contraction (18)
 constexpr int KL = DC / 32;                  // k-steps over the latent dims (16); the rest are rope dims
