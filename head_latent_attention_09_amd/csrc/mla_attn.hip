@@ -314,7 +314,7 @@ constexpr int P_BYTES = 32 * NW * TILE * 2;  // bf16 softmax weights of one tile
 constexpr int RING = 5;                      // score operand (tile) reads in flight per wave
 constexpr int QA = 2;                        // k-steps the query operand reads from LDS run ahead
 constexpr int DW = DC / NW;                  // output dims per wave in the value product
-constexpr float SLACK = 64.0f;               // log2 units a score may exceed the reference max
+constexpr float SLACK = 0x1p64f;             // bound on a segment's sum of weights 2^(s - m_ref)
 constexpr int LDS_QR = NBUF * TILE_BYTES;
 constexpr int LDS_P = LDS_QR + NW * QR_BYTES;
 constexpr int LDS_INV = LDS_P + 2 * P_BYTES;
@@ -662,7 +662,6 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
 
   float m_ref[2] = {0.f, 0.f};  // per owned head: reference max (log2 units)
   float lsum[2] = {0.f, 0.f};   // per owned head: this lane's part of the denominator
-  float ovm = -INFINITY;        // largest score minus reference seen by this lane
   f32x4 s0[2], s1[2];           // scores of two consecutive tiles (S^T blocks per 16 heads)
   bf16x8 kr[RING];              // score operand ring
   f32x16 o[NHB][4];
@@ -758,7 +757,6 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
       const int hb = p >> 1, r0 = 2 * (p & 1);
       const float x0 = sc[hb][r0] * a.scale_log2 - m_ref[hb];
       const float x1 = sc[hb][r0 + 1] * a.scale_log2 - m_ref[hb];
-      ovm = fmaxf(ovm, fmaxf(x0, x1));
       float w0 = __builtin_amdgcn_exp2f(x0), w1 = __builtin_amdgcn_exp2f(x1);
       opaque(w0);  // computed here, between the MFMAs, not where it is used
       opaque(w1);
@@ -840,24 +838,28 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
   // of the segment's first tile and the weights are 2^(x - m_ref). Keeping
   // the reference fixed keeps the output accumulator free of data-dependent
   // rescaling (a conditional rescale moves it out of the accumulation
-  // registers). If a later score exceeds m_ref by more than SLACK the
-  // exponent is clamped and the row is flagged; the first workgroup to flag
-  // row r recomputes the whole row with the generic running-max kernel into
-  // the final output, and the combine skips flagged rows. Scores would have
-  // to grow by more than 2^64 within one segment for that to happen.
+  // registers). A later score far above m_ref shows in the sum of weights:
+  // a segment whose sum reaches SLACK = 2^64 (or is inf or NaN) flags its
+  // row, and the first workgroup to flag row r recomputes the whole row with
+  // the generic running-max kernel into the final output; the combine skips
+  // flagged rows. Any score more than 64 (log2 units) above m_ref gives such
+  // a sum; below it the weights, sums and outputs stay far inside the range
+  // of bf16 and fp32.
   int le = lane;  // per-lane values of the epilogue stay here (see the tile loop)
   opaque(le);
   float lse_v[2] = {0.f, 0.f};
   if (owner) {
-    if (__any(ovm > SLACK) && le == 0) atomicOr(seg_flag, 1);
+    bool over = false;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       float l = lsum[hb];
       l += shfl_xor(l, le, 16);
       l += shfl_xor(l, le, 32);
+      over |= !(l < SLACK);  // also catches inf and NaN
       lse_v[hb] = (m_ref[hb] + __log2f(l)) * kLn2;
       if (le < 16) inv_s[wv * 32 + hb * 16 + le] = 1.0f / l;
     }
+    if (__any(over) && le == 0) atomicOr(seg_flag, 1);
   }
   __syncthreads();
   if (*seg_flag) {
