@@ -757,9 +757,7 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
       const int hb = p >> 1, r0 = 2 * (p & 1);
       const float x0 = sc[hb][r0] * a.scale_log2 - m_ref[hb];
       const float x1 = sc[hb][r0 + 1] * a.scale_log2 - m_ref[hb];
-      float w0 = __builtin_amdgcn_exp2f(x0), w1 = __builtin_amdgcn_exp2f(x1);
-      opaque(w0);  // computed here, between the MFMAs, not where it is used
-      opaque(w1);
+      const float w0 = __builtin_amdgcn_exp2f(x0), w1 = __builtin_amdgcn_exp2f(x1);
       bf16x2 q;
       q[0] = f32_to_bf16(w0);
       q[1] = f32_to_bf16(w1);
