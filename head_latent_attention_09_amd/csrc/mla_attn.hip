@@ -555,7 +555,7 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
   constexpr int H = 32 * NHB;
   const int len = a.pl.len[r];
   const int b = row_batch(a.map, r);
-  const bool owner = wv < NHB;  // the wave scores heads 32wv .. 32wv+31
+  const bool owner = NHB >= NW || wv < NHB;  // the wave scores heads 32wv .. 32wv+31 (known at 128 heads)
   // Waves without heads (fewer than 128) also load a query block and score
   // the first tile (results unused): every path into the tile loop then passes
   // the compiler's waits for the query registers.
