@@ -10,9 +10,9 @@ HBM before timing, and rotated over several independent copies so the
 
 Prints ONE JSON line. `value` is latent head-tokens attended per second
 (B*H*seq per step). `roofline` is for the dominant kernel (the latent
-attention kernel), timed with HIP events recorded on its own stream on every
-n-th timed step (--event-every, default 5: an event record costs about 6 us
-of stream time).
+attention kernel), timed with two HIP events passed with its launch on its own
+stream (they take the start and end of its dispatch) on every n-th timed step
+(--event-every, default 5: an evented launch adds about 5 us of stream time).
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
 workload on this host.
 
@@ -154,9 +154,11 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Each event record costs about 6 us of stream time (a barrier and a
-    # timestamp write between two kernels), so the attention kernel is timed
-    # on every n-th step of the timed region rather than on every step.
+    # An evented launch adds about 5 us of stream time, so the attention
+    # kernel is timed on every n-th step of the timed region rather than on
+    # every step. The dispatch start is taken when the dispatch is picked up,
+    # which can be while the planning kernel before it still runs (a few us
+    # of it fall inside the interval: the measured rate is a lower bound).
     every = max(1, args.event_every)
     attn_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(0, args.steps, every)]

@@ -13,6 +13,7 @@
 // per head.
 #include "mla_internal.h"
 
+#include <hip/hip_ext.h>
 #include <math.h>
 
 namespace mla {
@@ -43,8 +44,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(RowMap m, Plan pl, int H, in
   const int r0 = min(tid * chunk, R), r1 = min(r0 + chunk, R);
   if (tid == 0) nsplit = 0;
   int nt = 0, nr = 0, nz0 = 0;  // this thread's tiles, non-empty rows and empty rows
+  int n_first = 0;              // the first row's length stays in a register (one row per thread up to 1024 rows)
   for (int r = r0; r < r1; ++r) {
     int n = row_len(m, r);
+    if (r == r0) n_first = n;
     pl.len[r] = n;
     pl.flags[r] = 0;
     nt += (n + tile - 1) / tile;
@@ -81,8 +84,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(RowMap m, Plan pl, int H, in
     nz += z;
   }
   // list the empty rows (written at the end)
+  auto len_of = [&](int r) { return r == r0 ? n_first : pl.len[r]; };
   for (int r = r0, i = sz - nz0; r < r1; ++r)
-    if (pl.len[r] == 0 && i < 256) zrows[i++] = r;
+    if (len_of(r) == 0 && i < 256) zrows[i++] = r;
   // fixed cost per row only when rows are shorter on average than a worker's
   // share of the tiles (many rows per worker); longer rows are cut into about
   // equal pieces anyway, and every piece pays the fixed cost
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(RowMap m, Plan pl, int H, in
   }
   int base = (st - nt) + seg_cost * (sr - nr);  // first unit of this thread's rows
   for (int r = r0; r < r1; ++r) {
-    const int n = row_units((pl.len[r] + tile - 1) / tile, seg_cost);
+    const int n = row_units((len_of(r) + tile - 1) / tile, seg_cost);
     pl.cum[r] = base;
     const int s0 = base + seg_cost;  // first unit of the row's tiles
     if (n > 0 && s0 / per != (base + n - 1) / per) {
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(RowMap m, Plan pl, int H, in
   }
   if (nz > 256) {  // more empty rows than the list holds: each thread writes its own
     for (int r = r0; r < r1; ++r)
-      if (pl.len[r] == 0) {
+      if (len_of(r) == 0) {
         for (int i = 0; i < H * d_c; ++i) store_f32(out + (size_t)r * H * d_c + i, 0.f);
         if (lse)
           for (int h = 0; h < H; ++h) lse[(size_t)r * H + h] = -INFINITY;
@@ -1075,6 +1079,18 @@ int attn_tile_size(const AttnCall& c) { return use_mfma(c) ? mf::TILE : gn::TT; 
     if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP; \
   } while (0)
 
+// Launch of the attention kernel. With timing events the launch carries them
+// (no marker commands on the stream): they take the start and end times of
+// the kernel's dispatch.
+template <typename K, typename A>
+static void launch_timed(const AttnCall& c, K kernel, dim3 grid, dim3 block, const A& a) {
+  if (c.timing_events)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, c.stream, (hipEvent_t)c.timing_events[0],
+                          (hipEvent_t)c.timing_events[1], 0, a);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, c.stream, a);
+}
+
 template <typename T>
 static void launch_generic(const AttnCall& c, const Plan& pl) {
   gn::Args<T> a;
@@ -1089,7 +1105,7 @@ static void launch_generic(const AttnCall& c, const Plan& pl) {
   a.out = (T*)c.out;
   a.lse = c.lse;
   dim3 grid(c.G, (c.H + gn::HG - 1) / gn::HG);
-  hipLaunchKernelGGL(gn::attn_generic_kernel<T>, grid, dim3(gn::NT), 0, c.stream, a);
+  launch_timed(c, gn::attn_generic_kernel<T>, grid, dim3(gn::NT), a);
 }
 
 template <typename T>
@@ -1099,7 +1115,6 @@ static int launch_attention_t(const AttnCall& c) {
   Plan pl = plan_layout(c.ws, c.R, c.G, c.H, c.d_c, tile);
   hipLaunchKernelGGL(plan_kernel<T>, dim3(1), dim3(1024), 0, c.stream, c.map, pl, c.H, c.d_c, (T*)c.out, c.lse);
   MLA_LAUNCH_CHECK();
-  if (c.timing_events && hipEventRecord((hipEvent_t)c.timing_events[0], c.stream) != hipSuccess) return MLA_ERR_HIP;
   if (mfma) {
     mf::Args a;
     a.q = (const bf16*)c.q;
@@ -1113,24 +1128,23 @@ static int launch_attention_t(const AttnCall& c) {
     const dim3 grid(c.G), block(mf::NW * 64);
     if (c.map.mode != 2) {  // decode: every cache row read once
       switch (c.H / 32) {
-        case 1: hipLaunchKernelGGL((mf::attn_mfma_kernel<1, true>), grid, block, 0, c.stream, a); break;
-        case 2: hipLaunchKernelGGL((mf::attn_mfma_kernel<2, true>), grid, block, 0, c.stream, a); break;
-        case 3: hipLaunchKernelGGL((mf::attn_mfma_kernel<3, true>), grid, block, 0, c.stream, a); break;
-        default: hipLaunchKernelGGL((mf::attn_mfma_kernel<4, true>), grid, block, 0, c.stream, a); break;
+        case 1: launch_timed(c, mf::attn_mfma_kernel<1, true>, grid, block, a); break;
+        case 2: launch_timed(c, mf::attn_mfma_kernel<2, true>, grid, block, a); break;
+        case 3: launch_timed(c, mf::attn_mfma_kernel<3, true>, grid, block, a); break;
+        default: launch_timed(c, mf::attn_mfma_kernel<4, true>, grid, block, a); break;
       }
     } else {  // causal prefill: rows re-read by every later query
       switch (c.H / 32) {
-        case 1: hipLaunchKernelGGL((mf::attn_mfma_kernel<1, false>), grid, block, 0, c.stream, a); break;
-        case 2: hipLaunchKernelGGL((mf::attn_mfma_kernel<2, false>), grid, block, 0, c.stream, a); break;
-        case 3: hipLaunchKernelGGL((mf::attn_mfma_kernel<3, false>), grid, block, 0, c.stream, a); break;
-        default: hipLaunchKernelGGL((mf::attn_mfma_kernel<4, false>), grid, block, 0, c.stream, a); break;
+        case 1: launch_timed(c, mf::attn_mfma_kernel<1, false>, grid, block, a); break;
+        case 2: launch_timed(c, mf::attn_mfma_kernel<2, false>, grid, block, a); break;
+        case 3: launch_timed(c, mf::attn_mfma_kernel<3, false>, grid, block, a); break;
+        default: launch_timed(c, mf::attn_mfma_kernel<4, false>, grid, block, a); break;
       }
     }
   } else {
     launch_generic<T>(c, pl);
   }
   MLA_LAUNCH_CHECK();
-  if (c.timing_events && hipEventRecord((hipEvent_t)c.timing_events[1], c.stream) != hipSuccess) return MLA_ERR_HIP;
   {
     // at most min(R, G - 1) rows are cut by the G - 1 worker boundaries
     const unsigned max_split = (unsigned)(c.R < c.G ? c.R : c.G);

@@ -120,9 +120,10 @@ int mla_up_v(const void* out_lat, const void* w_uv, void* out,
  *   contents on entry are ignored. Concurrent calls need separate workspaces.
  * num_workers: attention workgroups to launch (0 = mla_default_workers()).
  *   Results do not depend on it beyond floating-point rounding.
- * timing_events: NULL, or a pointer to two hipEvent_t that are recorded on
- *   `stream` immediately before and after the attention kernel (for
- *   profiling; the planning and combine kernels fall outside them).
+ * timing_events: NULL, or a pointer to two hipEvent_t passed with the
+ *   attention kernel's launch on `stream`: they take the start and end times
+ *   of its dispatch (for profiling; the planning and combine kernels fall
+ *   outside them).
  * Limits: d_c <= 1024, d_c + d_r <= 1152, n_heads <= 65535,
  *   page_size >= 1 when paged.
  * ------------------------------------------------------------------------- */

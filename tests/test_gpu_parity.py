@@ -90,6 +90,24 @@ def test_decode_split_count_invariance(workers):
     check_decode(case, num_workers=workers, label="split invariance")
 
 
+@pytest.mark.parametrize("dtype", [G.BF16, G.F32])
+def test_decode_timing_events(dtype):
+    """Timing events passed with the attention launch: the results equal those
+    of a launch without them, and the events take a positive interval."""
+    case = G.decode_case(3, 128, 512, 64, [700, 33, 1000], dtype, seed=8)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    say(f"decode timing events: dtype={dtype}")
+    q = to_dev(case.q, dtype)
+    cache = to_dev(case.cache, dtype)
+    lens = torch.from_numpy(case.lens.astype(np.int32)).cuda()
+    out0, lse0 = M.latent_decode(q, cache, lens, case.d_c, case.kq_scale)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    out1, lse1 = M.latent_decode(q, cache, lens, case.d_c, case.kq_scale, timing_events=ev)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
+    assert ev[0].elapsed_time(ev[1]) > 0
+
+
 @pytest.mark.parametrize("workers", [200, 0])
 def test_decode_row_over_many_workers(workers):
     """One long row cut into one or two tiles per worker: the combine merges
