@@ -64,11 +64,11 @@ int mla_absorb_q(const void* q_nope, const void* q_pe, const void* w_uk, void* q
   if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
   if (n_tokens < 0 || n_heads <= 0 || d_nope <= 0 || d_c <= 0 || d_r < 0) return MLA_ERR_SHAPE;
   if (n_heads > 65535 || d_nope > 4096 || d_c > 4096 || d_r > 1024) return MLA_ERR_UNSUPPORTED;
+  if (n_tokens == 0) return MLA_OK;  // nothing to do; empty tensors may have NULL data
   if (!q_nope || !w_uk || !q || (d_r > 0 && !q_pe)) return MLA_ERR_NULL;
   const int es = elem_size(dtype);
   if (!aligned(q_nope, es) || !aligned(w_uk, es) || !aligned(q, es) || (q_pe && !aligned(q_pe, es)))
     return MLA_ERR_ALIGN;
-  if (n_tokens == 0) return MLA_OK;
   if (n_tokens * (int64_t)n_heads * (d_c + d_r) > ((int64_t)1 << 40)) return MLA_ERR_UNSUPPORTED;
   return launch_absorb(q_nope, q_pe, w_uk, q, n_tokens, n_heads, d_nope, d_c, d_r, dtype, (hipStream_t)stream);
 }
@@ -78,10 +78,10 @@ int mla_up_v(const void* out_lat, const void* w_uv, void* out, int64_t n_tokens,
   if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
   if (n_tokens < 0 || n_heads <= 0 || d_c <= 0 || d_v <= 0) return MLA_ERR_SHAPE;
   if (n_heads > 65535 || d_c > 4096 || d_v > 4096) return MLA_ERR_UNSUPPORTED;
+  if (n_tokens == 0) return MLA_OK;  // nothing to do; empty tensors may have NULL data
   if (!out_lat || !w_uv || !out) return MLA_ERR_NULL;
   const int es = elem_size(dtype);
   if (!aligned(out_lat, es) || !aligned(w_uv, es) || !aligned(out, es)) return MLA_ERR_ALIGN;
-  if (n_tokens == 0) return MLA_OK;
   if (n_tokens * (int64_t)n_heads * d_c > ((int64_t)1 << 40)) return MLA_ERR_UNSUPPORTED;
   return launch_up_v(out_lat, w_uv, out, n_tokens, n_heads, d_c, d_v, dtype, (hipStream_t)stream);
 }
@@ -125,6 +125,10 @@ int mla_latent_decode(const void* q, const void* latent_cache, const int32_t* se
                       size_t workspace_bytes, int num_workers, void* const* timing_events, void* stream) {
   int st = attn_dims_check(batch, n_heads, d_c, d_r);
   if (st != MLA_OK) return st;
+  if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (!std::isfinite(kq_scale)) return MLA_ERR_SCALE;
+  if (num_workers < 0 || (!block_table && cache_stride < 0)) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;  // nothing to do; empty tensors may have NULL data
   st = common_attn_checks(q, latent_cache, out_lat, lse, workspace, dtype, kq_scale);
   if (st != MLA_OK) return st;
   if (!seq_lens) return MLA_ERR_NULL;
@@ -138,8 +142,6 @@ int mla_latent_decode(const void* q, const void* latent_cache, const int32_t* se
     if (cache_stride < 0) return MLA_ERR_SHAPE;
     cap = cache_stride;
   }
-  if (num_workers < 0) return MLA_ERR_SHAPE;
-  if (batch == 0) return MLA_OK;
   if ((int64_t)batch * ((cap + tile_min - 1) / tile_min) > INT32_MAX / 2) return MLA_ERR_UNSUPPORTED;
   const int G = resolve_workers(num_workers);
   if (G <= 0) return G == 0 ? MLA_ERR_SHAPE : G;
@@ -178,11 +180,13 @@ int mla_latent_prefill_causal(const void* q, const void* latent_cache, int batch
   if ((int64_t)batch * s_q > INT32_MAX - 1) return MLA_ERR_UNSUPPORTED;
   int st = attn_dims_check(batch, n_heads, d_c, d_r);
   if (st != MLA_OK) return st;
-  st = common_attn_checks(q, latent_cache, out_lat, lse, workspace, dtype, kq_scale);
-  if (st != MLA_OK) return st;
+  if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (!std::isfinite(kq_scale)) return MLA_ERR_SCALE;
   if (num_workers < 0) return MLA_ERR_SHAPE;
   const int64_t rows = (int64_t)batch * s_q;
-  if (rows == 0) return MLA_OK;
+  if (rows == 0) return MLA_OK;  // nothing to do; empty tensors may have NULL data
+  st = common_attn_checks(q, latent_cache, out_lat, lse, workspace, dtype, kq_scale);
+  if (st != MLA_OK) return st;
   if (rows * ((s_kv + 15) / 16) > INT32_MAX / 2) return MLA_ERR_UNSUPPORTED;
   const int G = resolve_workers(num_workers);
   if (G <= 0) return G == 0 ? MLA_ERR_SHAPE : G;
@@ -215,10 +219,10 @@ int mla_lse_combine(const float* o_parts, const float* lse_parts, int n_parts, i
   if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
   if (n_parts <= 0 || rows < 0 || n_heads <= 0 || d_c <= 0) return MLA_ERR_SHAPE;
   if (n_parts > 4096 || d_c > 4096 || n_heads > 65535 || rows > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  if (rows == 0) return MLA_OK;  // nothing to do; empty tensors may have NULL data
   if (!o_parts || !lse_parts || !out) return MLA_ERR_NULL;
   if (!aligned(o_parts, 4) || !aligned(lse_parts, 4) || !aligned(out, elem_size(dtype)) || (lse && !aligned(lse, 4)))
     return MLA_ERR_ALIGN;
-  if (rows == 0) return MLA_OK;
   return launch_lse_combine(o_parts, lse_parts, n_parts, rows, n_heads, d_c, dtype, out, lse, (hipStream_t)stream);
 }
 

@@ -33,7 +33,8 @@
  *     returns an error has enqueued nothing, except MLA_ERR_HIP, after which
  *     the state of the outputs is unspecified.
  *   - Size arguments of value 0 in a batch-like dimension (tokens, batch,
- *     query rows) are valid and do nothing.
+ *     query rows) are valid and do nothing; the call's pointers are then
+ *     not checked (empty tensors may have NULL data).
  */
 #ifndef MLA_H
 #define MLA_H

@@ -53,6 +53,7 @@ def test_absorb_validation():
     assert _absorb(d_c=5000) == -4
     assert _absorb(q=ODD) == -6
     assert _absorb(N=0) == 0                   # nothing to do, no launch
+    assert _absorb(N=0, q_nope=None, q_pe=None, w_uk=None, q=None) == 0  # empty tensors: NULL data
 
 
 def _upv(**kw):
@@ -68,6 +69,7 @@ def test_up_v_validation():
     assert _upv(d_c=4097) == -4
     assert _upv(lat=FAKE + 2) == -6            # fp32 needs 4-byte alignment
     assert _upv(N=0) == 0
+    assert _upv(N=0, lat=None, w=None, out=None) == 0
 
 
 def _decode(**kw):
@@ -96,6 +98,8 @@ def test_decode_validation():
     assert _decode(ws_bytes=need - 1) == -5
     assert _decode(workers=-3) == -2
     assert _decode(B=0) == 0
+    assert _decode(B=0, q=None, cache=None, lens=None, out=None, lse=None, ws=None) == 0
+    assert _decode(B=0, dtype=5) == -3 and _decode(B=0, scale=math.nan) == -7 and _decode(B=0, H=0) == -2
 
 
 def test_prefill_validation():
@@ -110,6 +114,7 @@ def test_prefill_validation():
     assert call(scale=math.nan) == -7
     assert call(ws=None) == -5
     assert call(B=0) == 0 and call(S_q=0) == 0
+    assert call(B=0, q=None, cache=None, out=None, ws=None) == 0
     assert call(B=70000, S_q=70000) == -4
 
 
@@ -121,6 +126,7 @@ def test_lse_combine_validation():
                                      a["out"], None, None)
     assert call(P=0) == -2 and call(dtype=9) == -3 and call(o=None) == -1
     assert call(P=5000) == -4 and call(o=ODD) == -6 and call(R=0) == 0
+    assert call(R=0, o=None, l=None, out=None) == 0
 
 
 def test_workspace_formula():

@@ -125,6 +125,50 @@ def test_decode_paged_small(dtype):
     check_decode(case, num_workers=16, label="paged small")
 
 
+@pytest.mark.parametrize("page_size", [1, 24, 16])
+def test_decode_paged_page_sizes(page_size):
+    """Pages smaller than a tile or not a multiple of it (generic kernel), and
+    the smallest page the MFMA kernel takes (16 positions)."""
+    lens = [40, 0, 17, 1, 33]
+    case = G.decode_case(5, 128, 512, 64, lens, G.BF16, seed=60 + page_size, page_size=page_size)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    check_decode(case, num_workers=7, label=f"page size {page_size}")
+
+
+@pytest.mark.parametrize("dtype", [G.BF16, G.F32])
+def test_decode_largest_dims_generic(dtype):
+    """d_c = 1024 and d_c + d_r = 1152, the largest the generic kernel takes."""
+    case = G.decode_case(2, 3, 1024, 128, [70, 9], dtype, seed=71)
+    case.kq_scale = 1.0 / math.sqrt(1024 + 128)
+    check_decode(case, num_workers=4, label="largest dims")
+
+
+@pytest.mark.parametrize("H", [160, 40])
+def test_decode_heads_outside_mfma(H):
+    """bf16 with d_c=512, d_r=64 but a head count the MFMA kernel does not take."""
+    case = G.decode_case(2, H, 512, 64, [100, 31], G.BF16, seed=80 + H)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    check_decode(case, num_workers=9, label=f"H={H}")
+
+
+def test_decode_all_rows_empty():
+    """Every sequence empty: zeros and lse = -inf, no attention work."""
+    case = G.decode_case(4, 128, 512, 64, [0, 0, 0, 0], G.BF16, seed=90, cache_rows=16)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    got, glse = run_decode(case)
+    assert np.all(got == 0) and np.all(np.isneginf(glse))
+
+
+def test_decode_batch_zero():
+    """An empty batch is accepted and launches nothing."""
+    q = torch.zeros((0, 128, 576), dtype=torch.bfloat16, device="cuda")
+    cache = torch.zeros((0, 16, 576), dtype=torch.bfloat16, device="cuda")
+    lens = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    out, lse = M.latent_decode(q, cache, lens, 512, 0.1)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 128, 512) and lse.shape == (0, 128)
+
+
 def test_decode_odd_shapes_generic():
     """d_c, d_r, H outside the MFMA specialisation (generic kernel), bf16 and fp32."""
     for dtype in (G.BF16, G.F32):
