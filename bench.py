@@ -13,8 +13,9 @@ Prints ONE JSON line. `value` is latent head-tokens attended per second
 attention kernel), timed with two HIP events passed with its launch on its own
 stream (they take the start and end of its dispatch) on every n-th timed step
 (--event-every, default 5: an evented launch adds about 5 us of stream time).
-`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
-workload on this host.
+`entry_points_ms` gives each entry point's own time (median and min over
+blocks of back-to-back calls). `cpu_baseline` times the fp64 CPU oracle on a
+bounded sample of the same workload on this host.
 
     python bench.py [--steps K] [--warmup W] [--prefill] [--no-cpu-baseline]
 """
@@ -180,6 +181,17 @@ def main():
     attn_ms = [a.elapsed_time(b_) for a, b_ in attn_ev]
     attn_avg = float(np.mean(attn_ms))
 
+    # Per entry point: blocks of back-to-back calls between two events (the
+    # events' own cost is spread over the block); median and min over blocks.
+    entry = {
+        "latent_decode (plan + attention + combine)": time_entry(
+            torch, stream, lambda i: M.latent_decode(sets[i % len(sets)]["q"], sets[i % len(sets)]["cache"], lens,
+                                                     D_C, case.kq_scale, out=sets[i % len(sets)]["out"],
+                                                     lse=sets[i % len(sets)]["lse"], workspace=ws)),
+        "up_v (W_UV stays in the last-level cache between calls)": time_entry(
+            torch, stream, lambda i: M.up_v(sets[i % len(sets)]["out"], wuv, out=sets[i % len(sets)]["v"])),
+    }
+
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -212,18 +224,39 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "latent attention (mla::mf::attn_mfma_kernel<4, true>)",
-                     "avg_launch_ms": round(attn_avg, 5), "alg_bytes_per_launch": alg_bytes,
+                     "avg_launch_ms": round(attn_avg, 5), "median_launch_ms": round(float(np.median(attn_ms)), 5),
+                     "min_launch_ms": round(float(np.min(attn_ms)), 5), "alg_bytes_per_launch": alg_bytes,
                      "timed_launches": len(attn_ev)},
         "roofline_mfma": {"achieved": round(alg_flop / (attn_avg / 1e3) / 1e12, 1), "peak": BF16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(alg_flop / (attn_avg / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                           "alg_flop_per_launch": alg_flop},
         "wall_s_timed": round(wall, 3),
+        "entry_points_ms": entry,
     }
     if args.prefill:
         line["prefill"] = bench_prefill(M, G, torch, dev, args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def time_entry(torch, stream, call, per_block=20, blocks=5):
+    """Median and min over `blocks` of the mean time of `per_block` back-to-back
+    calls (ms per call)."""
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(blocks):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(per_block):
+            call(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) / per_block)
+    return {"median": round(float(np.median(res)), 5), "min": round(float(np.min(res)), 5),
+            "calls": per_block * blocks}
 
 
 def bench_prefill(M, G, torch, dev, args):
@@ -266,13 +299,24 @@ def bench_prefill(M, G, torch, dev, args):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in attn]))
+    stream = torch.cuda.current_stream()
+    entry = {
+        "absorb_q": time_entry(torch, stream, lambda i: M.absorb_q(qn, qp, wuk, out=q), per_block=3, blocks=3),
+        "latent_prefill_causal": time_entry(
+            torch, stream, lambda i: M.latent_prefill_causal(q.view(Bp, Sp, Hp, -1), cache, c.d_c, c.kq_scale,
+                                                             out=out, lse=lse, workspace=ws),
+            per_block=3, blocks=3),
+        "up_v": time_entry(torch, stream, lambda i: M.up_v(out.view(Bp * Sp, Hp, -1), wuv, out=v),
+                           per_block=3, blocks=3),
+    }
     pairs = Bp * Hp * Sp * (Sp + 1) // 2
     flop = pairs * (2 * c.W + 2 * c.d_c)
     return {"workload": "causal prefill B=2 S=4096 H=128 (absorb + attention + up_v)",
             "ms_per_step": round(ms, 4), "latent_tokens_per_s": round(pairs / (ms / 1e3), 1),
             "attention_ms": round(attn_ms, 4),
             "attention_mfma_tflops": round(flop / (attn_ms / 1e3) / 1e12, 1),
-            "attention_mfma_frac": round(flop / (attn_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            "attention_mfma_frac": round(flop / (attn_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "entry_points_ms": entry}
 
 
 if __name__ == "__main__":

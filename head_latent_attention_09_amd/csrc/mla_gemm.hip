@@ -26,8 +26,7 @@ constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
 __device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
 // rows of 16 chunks (256 B): [K,D]-stored W tile read by 4-row transposing loads
 __device__ __forceinline__ int swz16(int r) {
-  const int t = r & 3;
-  return t == 0 ? 0 : (t == 1 ? 6 : (t == 2 ? 10 : 12));
+  return (0xCA60 >> (4 * (r & 3))) & 15;  // 0, 6, 10, 12 for r % 4 = 0..3 (a shift, not a branch)
 }
 
 struct Args {
@@ -97,11 +96,15 @@ __global__ __launch_bounds__(NT, 2) void gemm_mfma_kernel(Args a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
+  // two K slices in flight: both stage buffers are filled up front, and a
+  // buffer is refilled as soon as every wave has read it
   issue_stage<TRANS_W>(a, smem, n0, h, j0, 0, lane, wv);
+  if (nk > 1) issue_stage<TRANS_W>(a, smem + STAGE_BYTES, n0, h, j0, BK, lane, wv);
   for (int kc = 0; kc < nk; ++kc) {
-    wait_all_vm();
-    barrier();
-    if (kc + 1 < nk) issue_stage<TRANS_W>(a, smem + ((kc + 1) & 1) * STAGE_BYTES, n0, h, j0, (kc + 1) * BK, lane, wv);
+    // this wave's loads of slice kc have landed (8 per slice, issued in order) ...
+    if (kc + 1 < nk) __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));
+    else wait_all_vm();
+    barrier();  // ... and every other wave's
     const char* sa = smem + (kc & 1) * STAGE_BYTES;
     const char* sb = sa + A_BYTES;
 #pragma unroll
@@ -137,25 +140,58 @@ __global__ __launch_bounds__(NT, 2) void gemm_mfma_kernel(Args a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
+    if (kc + 2 < nk) {
+      barrier();  // every wave is done with this buffer
+      issue_stage<TRANS_W>(a, smem + (kc & 1) * STAGE_BYTES, n0, h, j0, (kc + 2) * BK, lane, wv);
+    }
   }
-  // D layout: lane column = lane%32, rows 8(r/4) + 4g + r%4
+
+  // Output through LDS: the accumulator layout (lane column lane%32, rows
+  // 8(r/4) + 4g + r%4) would write 2 bytes per lane and store; staged, every
+  // store writes 16 bytes per lane and four whole 256-byte row segments per
+  // wave.
+  constexpr int OROW = BN * 2 + 16;  // 16 bytes of padding per row
+  static_assert(BM * OROW <= 2 * STAGE_BYTES, "output tile fits the stage buffers");
+  barrier();  // every wave is done reading the stage buffers
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int col = j0 + wn * 64 + j * 32 + (lane & 31);
+      const int col = wn * 64 + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t n = n0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (n < a.N) a.out[((size_t)n * a.H + h) * a.ldo + col] = f32_to_bf16(acc[i][j][r]);
+        const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        *(MLA_LDS bf16*)(smem + row * OROW + col * 2) = f32_to_bf16(acc[i][j][r]);
       }
     }
-  // absorb: copy q_pe into the tail of the query rows (once per row block)
+  barrier();
+#pragma unroll
+  for (int it = 0; it < BM * (BN / 8) / NT; ++it) {
+    const int idx = it * NT + threadIdx.x;
+    const int row = idx >> 4, ch = idx & 15;
+    const int64_t n = n0 + row;
+    if (n < a.N)
+      *(bf16x8*)(a.out + ((size_t)n * a.H + h) * a.ldo + j0 + ch * 8) =
+          *(const MLA_LDS bf16x8*)(smem + row * OROW + ch * 16);
+  }
+  // absorb: copy q_pe into the tail of the query rows (once per row block),
+  // 16 bytes at a time when the tail is a multiple of 8 values
   if (a.tail_src && blockIdx.y == 0) {
-    for (int idx = threadIdx.x; idx < BM * a.tail; idx += NT) {
-      const int row = idx / a.tail, k = idx - row * a.tail;
-      const int64_t n = n0 + row;
-      if (n < a.N) a.out[((size_t)n * a.H + h) * a.ldo + a.D + k] = a.tail_src[((size_t)n * a.H + h) * a.tail + k];
+    if ((a.tail & 7) == 0 && ((uintptr_t)a.tail_src & 15) == 0) {
+      const int tc = a.tail >> 3;
+      for (int idx = threadIdx.x; idx < BM * tc; idx += NT) {
+        const int row = idx / tc, c = idx - row * tc;
+        const int64_t n = n0 + row;
+        if (n < a.N)
+          *(bf16x8*)(a.out + ((size_t)n * a.H + h) * a.ldo + a.D + c * 8) =
+              *(const bf16x8*)(a.tail_src + ((size_t)n * a.H + h) * a.tail + c * 8);
+      }
+    } else {
+      for (int idx = threadIdx.x; idx < BM * a.tail; idx += NT) {
+        const int row = idx / a.tail, k = idx - row * a.tail;
+        const int64_t n = n0 + row;
+        if (n < a.N) a.out[((size_t)n * a.H + h) * a.ldo + a.D + k] = a.tail_src[((size_t)n * a.H + h) * a.tail + k];
+      }
     }
   }
 }

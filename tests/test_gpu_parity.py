@@ -355,7 +355,9 @@ def test_config5_sampled():
 
 
 @pytest.mark.parametrize("dtype,N,H,d_in,d_out", [
-    (G.BF16, 300, 4, 512, 128), (G.BF16, 64, 128, 512, 128), (G.F32, 5, 3, 20, 20), (G.BF16, 7, 2, 40, 24)])
+    (G.BF16, 300, 4, 512, 128), (G.BF16, 64, 128, 512, 128), (G.F32, 5, 3, 20, 20), (G.BF16, 7, 2, 40, 24),
+    (G.BF16, 1100, 64, 512, 128),   # 128x128 tiles, 8 K slices, ragged last row block
+    (G.BF16, 260, 4, 256, 256)])
 def test_up_v(dtype, N, H, d_in, d_out):
     say(f"up_v {dtype} N={N} H={H} {d_in}->{d_out}")
     c = G.gemm_case(N, H, d_in, d_out, dtype, seed=N, transpose_w=True)
@@ -365,7 +367,8 @@ def test_up_v(dtype, N, H, d_in, d_out):
 
 
 @pytest.mark.parametrize("dtype,N,H,d_nope,d_c,d_r", [
-    (G.BF16, 300, 4, 128, 512, 64), (G.BF16, 129, 2, 64, 256, 0), (G.F32, 3, 3, 20, 20, 0), (G.F32, 9, 2, 4, 6, 2)])
+    (G.BF16, 300, 4, 128, 512, 64), (G.BF16, 129, 2, 64, 256, 0), (G.F32, 3, 3, 20, 20, 0), (G.F32, 9, 2, 4, 6, 2),
+    (G.BF16, 700, 8, 256, 512, 64)])   # 4 K slices (buffers refilled), ragged last row block
 def test_absorb(dtype, N, H, d_nope, d_c, d_r):
     say(f"absorb {dtype} N={N} H={H} {d_nope}->{d_c} + {d_r}")
     c = G.gemm_case(N, H, d_nope, d_c, dtype, seed=N + 1, transpose_w=False)
