@@ -285,6 +285,220 @@ __global__ __launch_bounds__(NT, 1) void upv_resident_kernel(Args a, int ncb, in
     if (n < a.N) a.out[((size_t)n * a.H + h) * a.ldo + col] = f32_to_bf16(acc[r]);
   }
 }
+
+// ---------------------------------------------------------------------------
+// Query absorption with a short contraction (d_nope <= 128): a workgroup owns
+// one (head, 128-column block). Its W_UK block (K x 128) passes through LDS
+// once into registers (each wave keeps the B fragments of its 64 columns: 64
+// VGPRs at K=128), so the whole LDS serves a five-buffer ring of 64-row
+// q_nope blocks with four blocks in flight. Each 64x128 output block is
+// staged through the consumed ring buffer and stored as whole 256-byte row
+// segments. The q_pe tail of the query rows is copied at the end, split over
+// the column-block workgroups of a head. With K this short the per-tile
+// kernel waits for its first loads most of the time; streaming keeps loads
+// in flight across row blocks.
+// ---------------------------------------------------------------------------
+constexpr int ABM = 64;                        // rows per streamed block
+constexpr int ANB = 5;                         // ring buffers (four blocks in flight)
+constexpr int A_SLICE = ABM * BK * 2;          // 8 KiB: 64 rows x 64 K
+constexpr int A_BLOCK = 2 * A_SLICE;           // room for K <= 128
+constexpr int W_SLICE = BK * BN * 2;           // 16 KiB: 64 K rows x 128 columns
+constexpr int ABS_SMEM = ANB * A_BLOCK;        // 80 KiB: two workgroups per CU
+static_assert(ABM * BN * 2 <= A_BLOCK, "output block staged in a ring buffer");
+static_assert(2 * W_SLICE <= ABS_SMEM, "W_UK block passes through the ring");
+
+// vmcnt wait with a run-time count (a jump table of immediate waits)
+__device__ __forceinline__ void wait_vm_n(int n) {
+  switch (n) {
+#define MLA_G(k) \
+  case k:        \
+    __builtin_amdgcn_s_waitcnt(((k) & 15) | (7 << 4) | (15 << 8) | (((k) >> 4) << 14)); \
+    break;
+#define MLA_G8(k) MLA_G(k) MLA_G(k + 1) MLA_G(k + 2) MLA_G(k + 3) MLA_G(k + 4) MLA_G(k + 5) MLA_G(k + 6) MLA_G(k + 7)
+    MLA_G8(0) MLA_G8(8) MLA_G8(16) MLA_G8(24) MLA_G(32)
+#undef MLA_G8
+#undef MLA_G
+    default: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+  }
+}
+
+// Direct global->LDS load of 64 lanes x 16 bytes (lane l: gbase + voff to
+// LDS lds + 16 l), issued from inline asm: for the builtin the compiler waits
+// for every such load in flight before any LDS read, which would drain the
+// loads prefetched for later blocks. Completion is waited for explicitly.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(gbase), "s"(lds) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_u32(const void* p) { return (uint32_t)(uintptr_t)(const MLA_LDS char*)p; }
+
+// output staging: chunk c (8 columns) of row r at chunk c ^ (r & 15)
+__device__ __forceinline__ int ostage(int r, int col) {
+  return r * (BN * 2) + ((((col >> 3) ^ (r & 15))) << 4) + (col & 7) * 2;
+}
+
+__global__ __launch_bounds__(NT, 2) void absorb_stream_kernel(Args a, int parts) {
+  __shared__ __attribute__((aligned(1024))) char smem[ABS_SMEM];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int g = lane >> 5;
+  const int ncb = a.D / BN;
+  const int unit = blockIdx.x / parts, part = blockIdx.x - unit * parts;
+  const int h = unit / ncb, cb = unit - h * ncb;
+  const int j0 = cb * BN;
+  const int ns = a.K / BK;                // 1 or 2 K slices
+  const int64_t nrb = (a.N + ABM - 1) / ABM;
+  const int nt = (int)((nrb - part + parts - 1) / parts);  // row blocks of this workgroup: part + parts * i
+  const int wm = wv >> 1, wn = wv & 1;    // wave tile: rows 32wm.., columns 64wn..
+
+  // W_UK[h][k][j0 ..] through LDS (per slice 64 rows x 16 chunks, 4 loads per
+  // wave) into registers: B fragments of this wave's columns for every k-step
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl)
+    if (sl < ns)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ld = wv * 4 + i;
+        const int p = ld * 64 + lane;
+        const int row = p >> 4;
+        const int c = (p & 15) ^ swz16(row);
+        dma16(a.W + ((size_t)h * a.K + sl * BK) * a.D + j0, (uint32_t)((row * a.D + c * 8) * 2),
+              lds_u32(smem + sl * W_SLICE + ld * 1024));
+      }
+  wait_all_vm();
+  barrier();
+  bf16x8 bw[2][BK / 16][2];
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (sl >= ns) {
+          bw[sl][ks][j] = bf16x8{};
+          continue;
+        }
+        const char* sb = smem + sl * W_SLICE;
+        const int q16 = lane & 15, hf = (lane >> 4) & 1;
+        const int krow = 16 * ks + 8 * g + (q16 >> 2);
+        const int c = (wn * 64 + j * 32 + 16 * hf + (q16 & 3) * 4) >> 3;
+        const char* pa = sb + krow * 256 + ((c ^ swz16(krow)) * 16) + (q16 & 1) * 8;
+        const char* pb = sb + (krow + 4) * 256 + ((c ^ swz16(krow + 4)) * 16) + (q16 & 1) * 8;
+        s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)pa);
+        s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)pb);
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        s16x8 v8 = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+        bw[sl][ks][j] = __builtin_bit_cast(bf16x8, v8);
+      }
+  barrier();  // every wave holds its fragments: the ring may be overwritten
+
+  // A block t into ring buffer t % ANB: per slice 64 rows x 8 chunks, 2 loads per wave
+  auto issue_a = [&](int t) {
+    const int64_t r0 = (int64_t)(part + (int64_t)parts * t) * ABM;
+    char* st = smem + (t % ANB) * A_BLOCK;
+    const bf16* base = a.A + ((size_t)r0 * a.H + h) * a.K;  // row r0 of head h
+    const int64_t last = a.N - 1 - r0;                       // rows past the end re-read the last row
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+      if (sl < ns)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int ld = wv * 2 + i;
+          const int p = ld * 64 + lane;
+          const int row0 = p >> 3;
+          const int c = (p & 7) ^ swz8(row0);
+          const int row = row0 < last ? row0 : (int)last;
+          dma16(base, (uint32_t)(((size_t)row * a.H * a.K + sl * BK + c * 8) * 2),
+                lds_u32(st + sl * A_SLICE + ld * 1024));
+        }
+  };
+  constexpr int AHEAD_A = ANB - 1;  // blocks in flight
+  const int LA = 2 * ns;            // A loads per block and wave
+  constexpr int LS = 4;             // output stores per block and wave (64 rows x 256 B)
+  for (int t = 0; t < AHEAD_A && t < nt; ++t) issue_a(t);
+
+  for (int t = 0; t < nt; ++t) {
+    // every wave is done with the staging of block t-1 (ring buffer (t+4) % 5)
+    barrier();
+    if (t + AHEAD_A < nt) issue_a(t + AHEAD_A);
+    // this wave's memory operations issued after block t's loads: blocks
+    // t+1 .. t+4 that exist, and the stores of blocks max(0, t-4) .. t-1
+    int after = 0;
+#pragma unroll
+    for (int k = 1; k <= AHEAD_A; ++k) after += (t + k < nt ? LA : 0) + (t - k >= 0 ? LS : 0);
+    wait_vm_n(after);
+    barrier();  // block t complete for every wave
+    const char* sa = smem + (t % ANB) * A_BLOCK;
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+    const int ra = wm * 32 + (lane & 31);
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+      if (sl < ns)
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+          const bf16x8 af = *(const MLA_LDS bf16x8*)(sa + sl * A_SLICE + ra * 128 + (((2 * ks + g) ^ swz8(ra)) * 16));
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bw[sl][ks][j], acc[j], 0, 0, 0);
+        }
+    barrier();  // every wave is done reading block t: its buffer stages the output
+    char* so = smem + (t % ANB) * A_BLOCK;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        *(MLA_LDS bf16*)(so + ostage(row, col)) = f32_to_bf16(acc[j][r]);
+      }
+    }
+    barrier();
+    const int64_t r0 = (int64_t)(part + (int64_t)parts * t) * ABM;
+#pragma unroll
+    for (int it = 0; it < LS; ++it) {
+      const int idx = it * NT + threadIdx.x;
+      const int row = idx >> 4, ch = idx & 15;
+      const int64_t n = r0 + row;
+      const bf16x8 v = *(const MLA_LDS bf16x8*)(so + row * (BN * 2) + ((ch ^ (row & 15)) << 4));
+      if (n < a.N) *(bf16x8*)(a.out + ((size_t)n * a.H + h) * a.ldo + j0 + ch * 8) = v;
+    }
+  }
+
+  // q_pe into the tail of the query rows: the rows of this workgroup's row
+  // blocks are dealt round robin to the head's column-block workgroups, each
+  // row copied whole by consecutive threads (16 bytes each); four loads in
+  // flight per thread before their stores
+  if (a.tail_src) {
+    const int tc = a.tail >> 3;  // chunks per row (the tail is a multiple of 8 values)
+    const int64_t rows = (int64_t)nt * ABM;
+    const int64_t mine = rows > cb ? (rows - cb + ncb - 1) / ncb : 0;  // rows cb, cb + ncb, ...
+    const int64_t total = mine * tc;
+    for (int64_t w0 = threadIdx.x; w0 < total; w0 += (int64_t)NT * 4) {
+      bf16x8 v[4];
+      int64_t nn[4];
+      int cc[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t w = w0 + (int64_t)NT * u;
+        nn[u] = -1;
+        if (w < total) {
+          const int64_t j = w / tc;
+          cc[u] = (int)(w - j * tc);
+          const int64_t rr = cb + ncb * j;  // row of this workgroup's blocks
+          const int64_t t = rr / ABM;
+          const int64_t n = (int64_t)(part + (int64_t)parts * t) * ABM + (rr - t * ABM);
+          if (n < a.N) {
+            nn[u] = n;
+            v[u] = *(const bf16x8*)(a.tail_src + ((size_t)n * a.H + h) * a.tail + cc[u] * 8);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (nn[u] >= 0) *(bf16x8*)(a.out + ((size_t)nn[u] * a.H + h) * a.ldo + a.D + cc[u] * 8) = v[u];
+    }
+  }
+}
 }  // namespace gm
 
 // generic per-head product: one thread per output element, fp32 accumulation
@@ -342,6 +556,22 @@ int launch_absorb(const void* q_nope, const void* q_pe, const void* w_uk, void* 
   if (dtype == MLA_BF16 && mfma_ok(d_nope, d_c, ldo, q_nope, w_uk, q)) {
     gm::Args a{(const bf16*)q_nope, (const bf16*)w_uk, (bf16*)q, d_r > 0 ? (const bf16*)q_pe : nullptr,
                N, H, d_nope, d_c, ldo, d_r};
+    if (d_nope <= 2 * gm::BK && d_r % 8 == 0 && (d_r == 0 || al16(q_pe))) {
+      // one workgroup per (head, column block), or several splitting the row
+      // blocks when there are fewer than two per compute unit
+      int cus = mla_default_workers();
+      if (cus <= 0) cus = 256;
+      const int64_t units = (int64_t)H * (d_c / gm::BN);
+      const int64_t nrb = (N + gm::ABM - 1) / gm::ABM;
+      int64_t parts = (2 * (int64_t)cus + units - 1) / units;
+      if (parts > nrb) parts = nrb;
+      if (parts < 1) parts = 1;
+      if (units * parts <= INT32_MAX) {
+        hipLaunchKernelGGL(gm::absorb_stream_kernel, dim3((unsigned)(units * parts)), dim3(gm::NT), 0, s, a,
+                           (int)parts);
+        return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+      }
+    }
     dim3 grid((unsigned)((N + gm::BM - 1) / gm::BM), d_c / gm::BN, H);
     hipLaunchKernelGGL(gm::gemm_mfma_kernel<false>, grid, dim3(gm::NT), 0, s, a);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;

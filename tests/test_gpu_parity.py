@@ -368,7 +368,9 @@ def test_up_v(dtype, N, H, d_in, d_out):
 
 @pytest.mark.parametrize("dtype,N,H,d_nope,d_c,d_r", [
     (G.BF16, 300, 4, 128, 512, 64), (G.BF16, 129, 2, 64, 256, 0), (G.F32, 3, 3, 20, 20, 0), (G.F32, 9, 2, 4, 6, 2),
-    (G.BF16, 700, 8, 256, 512, 64)])   # 4 K slices (buffers refilled), ragged last row block
+    (G.BF16, 700, 8, 256, 512, 64),    # 128x128 tiles, 4 K slices (buffers refilled), ragged last row block
+    (G.BF16, 700, 8, 128, 512, 64),    # streaming kernel: W_UK resident, row blocks split over workgroups
+    (G.BF16, 1000, 3, 64, 128, 16)])   # streaming kernel, one K slice, one column block
 def test_absorb(dtype, N, H, d_nope, d_c, d_r):
     say(f"absorb {dtype} N={N} H={H} {d_nope}->{d_c} + {d_r}")
     c = G.gemm_case(N, H, d_nope, d_c, dtype, seed=N + 1, transpose_w=False)
