@@ -49,7 +49,6 @@ __global__ __launch_bounds__(1024) void plan_kernel(RowMap m, Plan pl, int H, in
     int n = row_len(m, r);
     if (r == r0) n_first = n;
     pl.len[r] = n;
-    pl.flags[r] = 0;
     nt += (n + tile - 1) / tile;
     nr += n > 0;
     nz0 += n == 0;
@@ -865,10 +864,13 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
   }
   __syncthreads();
   if (*seg_flag) {
-    __shared__ int claim;
-    if (threadIdx.x == 0) claim = atomicOr(a.pl.flags + r, 1) == 0;
-    __syncthreads();
-    if (claim) recompute_row(a, r, smem);
+    // Recompute the whole row into the final output; a part of a split row
+    // also marks its lse slots (NaN) so that the combine leaves the row as
+    // it is. Every flagged part of a row recomputes it: the writes are the
+    // same values.
+    if (!full)
+      for (int h = threadIdx.x; h < H; h += blockDim.x) a.pl.part_lse[(size_t)slot * H + h] = __builtin_nanf("");
+    recompute_row(a, r, smem);
     return;
   }
 
@@ -988,8 +990,8 @@ __device__ void combine_head(int n, PartFn part, int d_c, OutT* out, float* lse_
 // 0 in slot s0, part i > 0 in slot 2(w0 + i) (the row started before those
 // workers' ranges). Each thread issues the lse and partial loads of up to NP
 // parts at once, then merges them with a running maximum, so a workgroup
-// waits for memory twice (list entry, then data). Rows the attention kernel
-// recomputed (flagged) are already final.
+// waits for memory twice (list entry, then data). A row with a part whose
+// lse is NaN was recomputed by the attention kernel and is already final.
 template <typename OutT, int VEC>
 __global__ __launch_bounds__(256) void plan_combine_kernel(Plan pl, int H, int d_c, OutT* out, float* lse) {
   constexpr int NP = 4;
@@ -1002,7 +1004,7 @@ __global__ __launch_bounds__(256) void plan_combine_kernel(Plan pl, int H, int d
   const int item = blockIdx.x * 256 + threadIdx.x;
   if (item >= H * nq) return;
   const int h = item / nq, d = (item - h * nq) * VEC;
-  const int flagged = pl.flags[r];
+  bool marked = false;  // a part recomputed the row
   float mx = -INFINITY, ws = 0.f;
   float acc[VEC];
 #pragma unroll
@@ -1016,6 +1018,7 @@ __global__ __launch_bounds__(256) void plan_combine_kernel(Plan pl, int H, int d
       const int slot = i == 0 ? s0 : 2 * (w0 + i);
       l[j] = p0 + j < n ? pl.part_lse[(size_t)slot * H + h] : -INFINITY;
       v[j] = *(const vec_t*)((const OutT*)pl.part_o + ((size_t)slot * H + h) * d_c + d);
+      marked |= l[j] != l[j];
     }
     float m2 = mx;
 #pragma unroll
@@ -1034,7 +1037,7 @@ __global__ __launch_bounds__(256) void plan_combine_kernel(Plan pl, int H, int d
     }
     mx = m2;
   }
-  if (flagged) return;
+  if (marked) return;
   const float inv = ws > 0.f ? 1.0f / ws : 0.f;
   vec_t o;
 #pragma unroll

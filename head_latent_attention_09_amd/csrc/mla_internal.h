@@ -71,7 +71,6 @@ template <> __device__ __forceinline__ void store_f32<bf16>(bf16* p, float v) { 
 struct Plan {
   int32_t* cum;     // [R + 1]: exclusive prefix sum of units per row (cum[R] = total)
   int32_t* len;     // [R]: visible positions per row (clamped)
-  int32_t* flags;   // [R]: set when a row had to be recomputed (see the attention kernel)
   int32_t* split;   // [4 + 4G]: count, the fixed cost per row c, then per row cut by a worker boundary
                     //   {row, slot of its first part, its first worker, number of parts} (16-byte entries
                     //   from index 4)
@@ -85,10 +84,10 @@ struct Plan {
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// workspace layout: cum | len | flags | split | wrow | part_o | part_lse
+// workspace layout: cum | len | split | wrow | part_o | part_lse
 inline size_t plan_bytes(int64_t R, int G, int H, int d_c) {
   size_t b = align256(sizeof(int32_t) * (size_t)(R + 1));
-  b += 2 * align256(sizeof(int32_t) * (size_t)R);
+  b += align256(sizeof(int32_t) * (size_t)R);
   b += align256(sizeof(int32_t) * (size_t)(4 + 4 * G));
   b += align256(sizeof(int32_t) * (size_t)G);
   b += align256(sizeof(float) * (size_t)2 * G * H * d_c);
@@ -102,8 +101,6 @@ inline Plan plan_layout(void* ws, int R, int G, int H, int d_c, int tile) {
   pl.cum = (int32_t*)p;
   p += align256(sizeof(int32_t) * (size_t)(R + 1));
   pl.len = (int32_t*)p;
-  p += align256(sizeof(int32_t) * (size_t)R);
-  pl.flags = (int32_t*)p;
   p += align256(sizeof(int32_t) * (size_t)R);
   pl.split = (int32_t*)p;
   p += align256(sizeof(int32_t) * (size_t)(4 + 4 * G));

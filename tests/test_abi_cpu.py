@@ -130,16 +130,16 @@ def test_lse_combine_validation():
 
 
 def test_workspace_formula():
-    """Workspace = cum (R+1) + len (R) + flags (R) + split list (4 + 4G) +
+    """Workspace = cum (R+1) + len (R) + split list (4 + 4G) +
     first row per worker (G) int32, then 2G partial outputs [H, d_c] and 2G partial
     lse [H] in fp32, each region 256-byte aligned."""
     def a256(x):
         return (x + 255) // 256 * 256
     for B, H, d_c, G in [(64, 128, 512, 256), (1, 3, 20, 7), (128, 128, 512, 256)]:
-        want = (a256(4 * (B + 1)) + 2 * a256(4 * B) + a256(4 * (4 + 4 * G)) + a256(4 * G) + a256(4 * 2 * G * H * d_c)
+        want = (a256(4 * (B + 1)) + a256(4 * B) + a256(4 * (4 + 4 * G)) + a256(4 * G) + a256(4 * 2 * G * H * d_c)
                 + a256(4 * 2 * G * H))
         assert M.decode_workspace_bytes(B, H, d_c, G) == want
     assert M.prefill_workspace_bytes(2, 4096, 128, 512, 256) == (
-        a256(4 * 8193) + 2 * a256(4 * 8192) + a256(4 * (4 + 4 * 256)) + a256(4 * 256) + a256(4 * 2 * 256 * 128 * 512)
+        a256(4 * 8193) + a256(4 * 8192) + a256(4 * (4 + 4 * 256)) + a256(4 * 256) + a256(4 * 2 * 256 * 128 * 512)
         + a256(4 * 2 * 256 * 128))
     assert M.decode_workspace_bytes(-1, 4, 16, 8) == 0

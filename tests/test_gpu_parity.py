@@ -199,9 +199,11 @@ def test_decode_zero_query_is_mean():
         assert np.allclose(glse[b], math.log(case.lens[b]), atol=1e-3)
 
 
-def test_decode_large_logits_fixup():
+@pytest.mark.parametrize("workers", [4, 1])
+def test_decode_large_logits_fixup(workers):
     """Scores that rise by far more than 2^32 within a sequence (handled by the
-    recompute path of rows whose fixed softmax reference overflowed)."""
+    recompute path of rows whose fixed softmax reference overflowed): rows cut
+    over several workers (4) and rows finished by one worker (1)."""
     case = G.decode_case(2, 128, 512, 64, [600, 300], G.BF16, seed=13)
     case.kq_scale = 1.0 / math.sqrt(192)
     cache = G.to_f64(case.cache, G.BF16)
@@ -211,7 +213,7 @@ def test_decode_large_logits_fixup():
     q = G.to_f64(case.q, G.BF16)
     q[:, :, 512] = 40.0
     case.q = G.storage(q, G.BF16)
-    check_decode(case, num_workers=4, label="large logits")
+    check_decode(case, num_workers=workers, label="large logits")
 
 
 # ----------------------------------------------------------------------------
