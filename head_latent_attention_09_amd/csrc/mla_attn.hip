@@ -149,6 +149,71 @@ __device__ __forceinline__ int page_of(const RowMap& m, int b, int t) {
   return p < 0 ? 0 : (p >= m.num_pages ? m.num_pages - 1 : p);
 }
 
+// Planning inside a kernel, for batches of at most SELF_MAX_R rows: every
+// workgroup of 256 threads derives the same unit prefix sums as plan_kernel
+// from the row lengths, into LDS (cum_s [R + 1], len_s [R]); returns the
+// fixed cost per row and the total. This spares a decode call the planning
+// kernel and its launch; nothing of the plan is then kept in the workspace.
+constexpr int SELF_MAX_R = 256;
+__device__ void self_plan(const RowMap& m, int R, int G, int tile, int* cum_s, int* len_s, int& seg_cost,
+                          int& total) {
+  __shared__ int wt[4], wr[4];  // per-wave totals of tiles and non-empty rows
+  constexpr int CH = SELF_MAX_R / 256;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int r0 = tid * CH;
+  int tl[CH];
+  int nt = 0, nr = 0;
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int r = r0 + j;
+    int n = 0;
+    if (r < R) {
+      n = row_len(m, r);
+      len_s[r] = n;
+    }
+    tl[j] = (n + tile - 1) / tile;
+    nt += tl[j];
+    nr += n > 0;
+  }
+  int st = nt, sr = nr;  // inclusive scans: within the wave, then over the 4 wave totals
+  for (int o = 1; o < 64; o <<= 1) {
+    const int yt = __shfl_up(st, o), yr = __shfl_up(sr, o);
+    if (lane >= o) {
+      st += yt;
+      sr += yr;
+    }
+  }
+  if (lane == 63) {
+    wt[wid] = st;
+    wr[wid] = sr;
+  }
+  __syncthreads();
+  int all_t = 0, all_r = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < wid) {
+      st += wt[i];
+      sr += wr[i];
+    }
+    all_t += wt[i];
+    all_r += wr[i];
+  }
+  const int c = all_r > 0 && all_t / all_r < plan_per_worker(all_t, G) ? SEG_COST : 0;
+  int base = (st - nt) + c * (sr - nr);
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int r = r0 + j;
+    if (r < R) {
+      cum_s[r] = base;
+      base += row_units(tl[j], c);
+    }
+  }
+  if (tid == 0) cum_s[R] = all_t + c * all_r;
+  __syncthreads();
+  seg_cost = __builtin_amdgcn_readfirstlane(c);  // the same in every lane
+  total = __builtin_amdgcn_readfirstlane(all_t + c * all_r);
+}
+
 // ===========================================================================
 // generic attention (fp32 or bf16 storage, any d_c <= 1024, d_c + d_r <= 1152)
 // fp32 arithmetic on the vector ALUs; 8 heads per workgroup, 16-position tiles.
@@ -169,13 +234,12 @@ struct Args {
 };
 
 template <typename T>
-__device__ void attend_segment(const Args<T>& a, int r, int lt0, int lt1, bool full, int slot, int h0,
+__device__ void attend_segment(const Args<T>& a, int r, int len, int lt0, int lt1, bool full, int slot, int h0,
                                float* tile, float* qs, float* ps, float* alpha_s, float* stat_s,
                                float& m_run, float& l_run) {
   const int tid = threadIdx.x;
   const int W = a.d_c + a.d_r, WP = W + 1, H = a.H, d_c = a.d_c;
   const int nh = min(HG, H - h0);
-  const int len = a.pl.len[r];
   const int b = row_batch(a.map, r);
   __syncthreads();
   for (int i = tid; i < HG * W; i += NT) {
@@ -290,7 +354,8 @@ __global__ __launch_bounds__(NT) void attn_generic_kernel(Args<T> a) {
     if (c0 >= t_end) break;
     Segment sg;
     if (!plan_segment(c0, c1, seg_cost, t_begin, t_end, w, per, sg)) continue;
-    attend_segment<T>(a, r, sg.lt0, sg.lt1, sg.full, sg.slot, h0, tile, qs, ps, alpha_s, stat_s, m_run, l_run);
+    attend_segment<T>(a, r, a.pl.len[r], sg.lt0, sg.lt1, sg.full, sg.slot, h0, tile, qs, ps, alpha_s, stat_s, m_run,
+                      l_run);
   }
 }
 }  // namespace gn
@@ -527,7 +592,7 @@ __device__ __forceinline__ void issue_tile(const TileSrc& s, char* buf, int lx, 
 
 // Whole-row recompute with the generic kernel (running max with rescaling),
 // writing the final result; the tile ring is reused as its scratch.
-__device__ void recompute_row(const Args& a, int r, char* smem) {
+__device__ void recompute_row(const Args& a, int r, int len, char* smem) {
   gn::Args<bf16> ga;
   ga.q = a.q;
   ga.cache = a.cache;
@@ -545,18 +610,16 @@ __device__ void recompute_row(const Args& a, int r, char* smem) {
   float* alpha_s = ps + gn::HG * gn::TT;
   float* stat_s = alpha_s + gn::HG;
   float m_run = -INFINITY, l_run = 0.f;
-  const int len = a.pl.len[r];
   for (int h0 = 0; h0 < a.H; h0 += gn::HG)
-    gn::attend_segment<bf16>(ga, r, 0, (len + gn::TT - 1) / gn::TT, true, 0, h0, tile, qs, ps, alpha_s, stat_s,
-                             m_run, l_run);
+    gn::attend_segment<bf16>(ga, r, len, 0, (len + gn::TT - 1) / gn::TT, true, 0, h0, tile, qs, ps, alpha_s,
+                             stat_s, m_run, l_run);
   __syncthreads();
 }
 
 template <int NHB, bool STREAM>
-__device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, int lt1, bool full, int slot,
+__device__ __forceinline__ void attend_segment(const Args& a, int r, int len, int lt0, int lt1, bool full, int slot,
                                                char* smem, int* seg_flag, int lane, int wv) {
   constexpr int H = 32 * NHB;
-  const int len = a.pl.len[r];
   const int b = row_batch(a.map, r);
   const bool owner = NHB >= NW || wv < NHB;  // the wave scores heads 32wv .. 32wv+31 (known at 128 heads)
   // Waves without heads (fewer than 128) also load a query block and score
@@ -870,7 +933,7 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
     // same values.
     if (!full)
       for (int h = threadIdx.x; h < H; h += blockDim.x) a.pl.part_lse[(size_t)slot * H + h] = __builtin_nanf("");
-    recompute_row(a, r, smem);
+    recompute_row(a, r, len, smem);
     return;
   }
 
@@ -923,26 +986,48 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int lt0, in
   }
 }
 
-template <int NHB, bool STREAM>
+// SELF: the workgroup plans for itself (self_plan) instead of reading the
+// planning kernel's results.
+template <int NHB, bool STREAM, bool SELF>
 __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(Args a) {
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   __shared__ int seg_flag;
+  __shared__ int cum_s[SELF ? SELF_MAX_R + 1 : 1], len_s[SELF ? SELF_MAX_R : 1];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int G = a.pl.G;
+  const int G = a.pl.G, R = a.pl.R;
   const int w = xcd_worker(blockIdx.x, G);
-  const int total = a.pl.cum[a.pl.R];
-  const int seg_cost = a.pl.split[1];
+  int total, seg_cost;
+  if constexpr (SELF) {
+    self_plan(a.map, R, G, TILE, cum_s, len_s, seg_cost, total);
+  } else {
+    total = a.pl.cum[R];
+    seg_cost = a.pl.split[1];
+  }
   const int per = plan_per_worker(total, G);
   const int t_begin = w * per;
   if (t_begin >= total) return;
   const int t_end = min(t_begin + per, total);
-  for (int r = a.pl.wrow[w]; r < a.pl.R; ++r) {
-    const int c0 = a.pl.cum[r], c1 = a.pl.cum[r + 1];
+  int first;  // the row holding unit t_begin
+  if constexpr (SELF) {
+    int lo = 0, hi = R;  // largest r with cum_s[r] <= t_begin
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cum_s[mid] <= t_begin) lo = mid;
+      else hi = mid - 1;
+    }
+    first = __builtin_amdgcn_readfirstlane(lo);  // LDS values are the same in every lane
+  } else {
+    first = a.pl.wrow[w];
+  }
+  for (int r = first; r < R; ++r) {
+    const int c0 = SELF ? __builtin_amdgcn_readfirstlane(cum_s[r]) : a.pl.cum[r];
+    const int c1 = SELF ? __builtin_amdgcn_readfirstlane(cum_s[r + 1]) : a.pl.cum[r + 1];
     if (c0 >= t_end) break;
     Segment sg;
     if (!plan_segment(c0, c1, seg_cost, t_begin, t_end, w, per, sg)) continue;
-    attend_segment<NHB, STREAM>(a, r, sg.lt0, sg.lt1, sg.full, sg.slot, smem, &seg_flag, lane, wv);
+    const int len = SELF ? __builtin_amdgcn_readfirstlane(len_s[r]) : a.pl.len[r];
+    attend_segment<NHB, STREAM>(a, r, len, sg.lt0, sg.lt1, sg.full, sg.slot, smem, &seg_flag, lane, wv);
   }
 }
 }  // namespace mf
@@ -992,18 +1077,13 @@ __device__ void combine_head(int n, PartFn part, int d_c, OutT* out, float* lse_
 // parts at once, then merges them with a running maximum, so a workgroup
 // waits for memory twice (list entry, then data). A row with a part whose
 // lse is NaN was recomputed by the attention kernel and is already final.
+// Merge of the n parts of split row r for one item (VEC dims d.. of head h):
+// part 0 in slot s0, part i > 0 in slot 2(w0 + i).
 template <typename OutT, int VEC>
-__global__ __launch_bounds__(256) void plan_combine_kernel(Plan pl, int H, int d_c, OutT* out, float* lse) {
+__device__ __forceinline__ void merge_item(const Plan& pl, int H, int d_c, int r, int s0, int w0, int n, int h,
+                                           int d, OutT* out, float* lse) {
   constexpr int NP = 4;
   typedef OutT vec_t __attribute__((ext_vector_type(VEC)));
-  const int k = blockIdx.y;
-  const int4 e = *(const int4*)(pl.split + 4 + 4 * k);
-  if (k >= pl.split[0]) return;
-  const int r = e.x, s0 = e.y, w0 = e.z, n = e.w;
-  const int nq = d_c / VEC;
-  const int item = blockIdx.x * 256 + threadIdx.x;
-  if (item >= H * nq) return;
-  const int h = item / nq, d = (item - h * nq) * VEC;
   bool marked = false;  // a part recomputed the row
   float mx = -INFINITY, ws = 0.f;
   float acc[VEC];
@@ -1049,6 +1129,50 @@ __global__ __launch_bounds__(256) void plan_combine_kernel(Plan pl, int H, int d
   }
   *(vec_t*)(out + ((size_t)r * H + h) * d_c + d) = o;
   if (lse && d == 0) lse[(size_t)r * H + h] = ws > 0.f ? mx + __logf(ws) : -INFINITY;
+}
+
+template <typename OutT, int VEC>
+__global__ __launch_bounds__(256) void plan_combine_kernel(Plan pl, int H, int d_c, OutT* out, float* lse) {
+  const int k = blockIdx.y;
+  const int4 e = *(const int4*)(pl.split + 4 + 4 * k);
+  if (k >= pl.split[0]) return;
+  const int nq = d_c / VEC;
+  const int item = blockIdx.x * 256 + threadIdx.x;
+  if (item >= H * nq) return;
+  const int h = item / nq, d = (item - h * nq) * VEC;
+  merge_item<OutT, VEC>(pl, H, d_c, e.x, e.y, e.z, e.w, h, d, out, lse);
+}
+
+// Combine of a self-planned call: workgroup (x, r) plans as the attention
+// kernel did, then handles items 256x .. 256x+255 of row r: zeros and
+// lse = -inf for an empty row, the merge for a row cut by worker boundaries,
+// nothing for a row one worker finished.
+template <typename OutT, int VEC>
+__global__ __launch_bounds__(256) void self_combine_kernel(RowMap m, Plan pl, int H, int d_c, OutT* out,
+                                                           float* lse) {
+  __shared__ int cum_s[SELF_MAX_R + 1], len_s[SELF_MAX_R];
+  int seg_cost, total;
+  self_plan(m, pl.R, pl.G, pl.tile, cum_s, len_s, seg_cost, total);
+  typedef OutT vec_t __attribute__((ext_vector_type(VEC)));
+  const int r = blockIdx.y;
+  const int nq = d_c / VEC;
+  const int item = blockIdx.x * 256 + threadIdx.x;
+  if (item >= H * nq) return;
+  const int h = item / nq, d = (item - h * nq) * VEC;
+  if (len_s[r] == 0) {
+    vec_t z;
+#pragma unroll
+    for (int x = 0; x < VEC; ++x) z[x] = (OutT)0.f;
+    *(vec_t*)(out + ((size_t)r * H + h) * d_c + d) = z;
+    if (lse && d == 0) lse[(size_t)r * H + h] = -INFINITY;
+    return;
+  }
+  const int per = plan_per_worker(total, pl.G);
+  const int base = cum_s[r], n = cum_s[r + 1] - base;
+  const int s0 = base + seg_cost;  // first unit of the row's tiles
+  const int w0 = s0 / per, w1 = (base + n - 1) / per;
+  if (w0 == w1) return;  // finished by one worker
+  merge_item<OutT, VEC>(pl, H, d_c, r, plan_slot(w0, s0, per), w0, w1 - w0 + 1, h, d, out, lse);
 }
 
 template <typename OutT>
@@ -1116,8 +1240,15 @@ static int launch_attention_t(const AttnCall& c) {
   const bool mfma = use_mfma(c);
   const int tile = mfma ? mf::TILE : gn::TT;
   Plan pl = plan_layout(c.ws, c.R, c.G, c.H, c.d_c, tile);
-  hipLaunchKernelGGL(plan_kernel<T>, dim3(1), dim3(1024), 0, c.stream, c.map, pl, c.H, c.d_c, (T*)c.out, c.lse);
-  MLA_LAUNCH_CHECK();
+  constexpr int VEC = 16 / (int)sizeof(T);
+  const bool vec_out = c.d_c % VEC == 0 && aligned16(c.out);
+  // decode batches of up to SELF_MAX_R rows on the MFMA kernel plan inside
+  // the attention and combine kernels (no planning kernel)
+  const bool self = mfma && c.map.mode != 2 && c.R <= SELF_MAX_R && vec_out;
+  if (!self) {
+    hipLaunchKernelGGL(plan_kernel<T>, dim3(1), dim3(1024), 0, c.stream, c.map, pl, c.H, c.d_c, (T*)c.out, c.lse);
+    MLA_LAUNCH_CHECK();
+  }
   if (mfma) {
     mf::Args a;
     a.q = (const bf16*)c.q;
@@ -1129,30 +1260,40 @@ static int launch_attention_t(const AttnCall& c) {
     a.out = (bf16*)c.out;
     a.lse = c.lse;
     const dim3 grid(c.G), block(mf::NW * 64);
-    if (c.map.mode != 2) {  // decode: every cache row read once
+    if (self) {  // decode: every cache row read once
       switch (c.H / 32) {
-        case 1: launch_timed(c, mf::attn_mfma_kernel<1, true>, grid, block, a); break;
-        case 2: launch_timed(c, mf::attn_mfma_kernel<2, true>, grid, block, a); break;
-        case 3: launch_timed(c, mf::attn_mfma_kernel<3, true>, grid, block, a); break;
-        default: launch_timed(c, mf::attn_mfma_kernel<4, true>, grid, block, a); break;
+        case 1: launch_timed(c, mf::attn_mfma_kernel<1, true, true>, grid, block, a); break;
+        case 2: launch_timed(c, mf::attn_mfma_kernel<2, true, true>, grid, block, a); break;
+        case 3: launch_timed(c, mf::attn_mfma_kernel<3, true, true>, grid, block, a); break;
+        default: launch_timed(c, mf::attn_mfma_kernel<4, true, true>, grid, block, a); break;
+      }
+    } else if (c.map.mode != 2) {
+      switch (c.H / 32) {
+        case 1: launch_timed(c, mf::attn_mfma_kernel<1, true, false>, grid, block, a); break;
+        case 2: launch_timed(c, mf::attn_mfma_kernel<2, true, false>, grid, block, a); break;
+        case 3: launch_timed(c, mf::attn_mfma_kernel<3, true, false>, grid, block, a); break;
+        default: launch_timed(c, mf::attn_mfma_kernel<4, true, false>, grid, block, a); break;
       }
     } else {  // causal prefill: rows re-read by every later query
       switch (c.H / 32) {
-        case 1: launch_timed(c, mf::attn_mfma_kernel<1, false>, grid, block, a); break;
-        case 2: launch_timed(c, mf::attn_mfma_kernel<2, false>, grid, block, a); break;
-        case 3: launch_timed(c, mf::attn_mfma_kernel<3, false>, grid, block, a); break;
-        default: launch_timed(c, mf::attn_mfma_kernel<4, false>, grid, block, a); break;
+        case 1: launch_timed(c, mf::attn_mfma_kernel<1, false, false>, grid, block, a); break;
+        case 2: launch_timed(c, mf::attn_mfma_kernel<2, false, false>, grid, block, a); break;
+        case 3: launch_timed(c, mf::attn_mfma_kernel<3, false, false>, grid, block, a); break;
+        default: launch_timed(c, mf::attn_mfma_kernel<4, false, false>, grid, block, a); break;
       }
     }
   } else {
     launch_generic<T>(c, pl);
   }
   MLA_LAUNCH_CHECK();
-  {
+  if (self) {
+    dim3 cgrid((unsigned)((c.H * (c.d_c / VEC) + 255) / 256), (unsigned)c.R);
+    hipLaunchKernelGGL((self_combine_kernel<T, VEC>), cgrid, dim3(256), 0, c.stream, c.map, pl, c.H, c.d_c,
+                       (T*)c.out, c.lse);
+  } else {
     // at most min(R, G - 1) rows are cut by the G - 1 worker boundaries
     const unsigned max_split = (unsigned)(c.R < c.G ? c.R : c.G);
-    constexpr int VEC = 16 / (int)sizeof(T);
-    if (c.d_c % VEC == 0 && aligned16(c.out)) {
+    if (vec_out) {
       dim3 cgrid((unsigned)((c.H * (c.d_c / VEC) + 255) / 256), max_split);
       hipLaunchKernelGGL((plan_combine_kernel<T, VEC>), cgrid, dim3(256), 0, c.stream, pl, c.H, c.d_c, (T*)c.out,
                          c.lse);
@@ -1161,8 +1302,8 @@ static int launch_attention_t(const AttnCall& c) {
       hipLaunchKernelGGL((plan_combine_kernel<T, 1>), cgrid, dim3(256), 0, c.stream, pl, c.H, c.d_c, (T*)c.out,
                          c.lse);
     }
-    MLA_LAUNCH_CHECK();
   }
+  MLA_LAUNCH_CHECK();
   return MLA_OK;
 }
 

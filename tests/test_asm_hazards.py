@@ -26,7 +26,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "head_latent_attention_09_amd", "csrc", "mla_attn.hip")
 HIPCC = "/opt/rocm/bin/hipcc"
-KERNELS = [f"_ZN3mla2mf16attn_mfma_kernelILi{n}ELb{s}EEEvNS0_4ArgsE" for n in (1, 2, 3, 4) for s in (0, 1)]
+KERNELS = [f"_ZN3mla2mf16attn_mfma_kernelILi{n}ELb{s}ELb{p}EEEvNS0_4ArgsE"
+           for n in (1, 2, 3, 4) for s, p in ((0, 0), (1, 0), (1, 1))]
 PRE_WAIT = 2      # VALU write of a VGPR -> MFMA read of it
 POST_WAIT = 18    # 16x16x32 MFMA result -> any other access
 

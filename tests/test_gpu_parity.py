@@ -108,6 +108,15 @@ def test_decode_timing_events(dtype):
     assert ev[0].elapsed_time(ev[1]) > 0
 
 
+def test_decode_batch_planned_by_kernel():
+    """More rows than the attention kernel plans for itself (256): the MFMA
+    kernel then reads the planning kernel's results."""
+    lens = np.random.default_rng(5).integers(0, 41, 300)
+    case = G.decode_case(300, 32, 512, 64, lens, G.BF16, seed=55)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    check_decode(case, label="300 rows")
+
+
 @pytest.mark.parametrize("workers", [200, 0])
 def test_decode_row_over_many_workers(workers):
     """One long row cut into one or two tiles per worker: the combine merges
