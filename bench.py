@@ -223,7 +223,7 @@ def main():
                    "cache": "dense", "workers": G_workers, "rotated_copies": args.copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "latent attention (mla::mf::attn_mfma_kernel<4, true>)",
+                     "kernel": "latent attention (mla::mf::attn_mfma_kernel<4, true, true>)",
                      "avg_launch_ms": round(attn_avg, 5), "median_launch_ms": round(float(np.median(attn_ms)), 5),
                      "min_launch_ms": round(float(np.min(attn_ms)), 5), "alg_bytes_per_launch": alg_bytes,
                      "timed_launches": len(attn_ev)},
