@@ -153,7 +153,8 @@ __device__ __forceinline__ int page_of(const RowMap& m, int b, int t) {
 // workgroup of 256 threads derives the same unit prefix sums as plan_kernel
 // from the row lengths, into LDS (cum_s [R + 1], len_s [R]); returns the
 // fixed cost per row and the total. This spares a decode call the planning
-// kernel and its launch; nothing of the plan is then kept in the workspace.
+// kernel and its launch; the first attention workgroup stores the prefix
+// sums, lengths and fixed cost for the combine kernel.
 constexpr int SELF_MAX_R = 256;
 __device__ void self_plan(const RowMap& m, int R, int G, int tile, int* cum_s, int* len_s, int& seg_cost,
                           int& total) {
@@ -1000,6 +1001,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(Args a) {
   int total, seg_cost;
   if constexpr (SELF) {
     self_plan(a.map, R, G, TILE, cum_s, len_s, seg_cost, total);
+    if (blockIdx.x == 0) {  // the combine kernel reads the plan of the rows from here
+      for (int r = threadIdx.x; r <= R; r += blockDim.x) {
+        a.pl.cum[r] = cum_s[r];
+        if (r < R) a.pl.len[r] = len_s[r];
+      }
+      if (threadIdx.x == 0) a.pl.split[1] = seg_cost;
+    }
   } else {
     total = a.pl.cum[R];
     seg_cost = a.pl.split[1];
@@ -1143,23 +1151,21 @@ __global__ __launch_bounds__(256) void plan_combine_kernel(Plan pl, int H, int d
   merge_item<OutT, VEC>(pl, H, d_c, e.x, e.y, e.z, e.w, h, d, out, lse);
 }
 
-// Combine of a self-planned call: workgroup (x, r) plans as the attention
-// kernel did, then handles items 256x .. 256x+255 of row r: zeros and
-// lse = -inf for an empty row, the merge for a row cut by worker boundaries,
-// nothing for a row one worker finished.
+// Combine of a self-planned call: workgroup (x, r) reads row r's plan, which
+// the first attention workgroup stored (prefix sums, length, fixed cost), and
+// handles items 256x .. 256x+255 of the row: zeros and lse = -inf for an empty
+// row, the merge for a row cut by worker boundaries, nothing for a row one
+// worker finished.
 template <typename OutT, int VEC>
-__global__ __launch_bounds__(256) void self_combine_kernel(RowMap m, Plan pl, int H, int d_c, OutT* out,
-                                                           float* lse) {
-  __shared__ int cum_s[SELF_MAX_R + 1], len_s[SELF_MAX_R];
-  int seg_cost, total;
-  self_plan(m, pl.R, pl.G, pl.tile, cum_s, len_s, seg_cost, total);
+__global__ __launch_bounds__(256) void self_combine_kernel(Plan pl, int H, int d_c, OutT* out, float* lse) {
   typedef OutT vec_t __attribute__((ext_vector_type(VEC)));
   const int r = blockIdx.y;
   const int nq = d_c / VEC;
   const int item = blockIdx.x * 256 + threadIdx.x;
   if (item >= H * nq) return;
   const int h = item / nq, d = (item - h * nq) * VEC;
-  if (len_s[r] == 0) {
+  const int base = pl.cum[r], n = pl.cum[r + 1] - base, total = pl.cum[pl.R], seg_cost = pl.split[1];
+  if (pl.len[r] == 0) {
     vec_t z;
 #pragma unroll
     for (int x = 0; x < VEC; ++x) z[x] = (OutT)0.f;
@@ -1168,7 +1174,6 @@ __global__ __launch_bounds__(256) void self_combine_kernel(RowMap m, Plan pl, in
     return;
   }
   const int per = plan_per_worker(total, pl.G);
-  const int base = cum_s[r], n = cum_s[r + 1] - base;
   const int s0 = base + seg_cost;  // first unit of the row's tiles
   const int w0 = s0 / per, w1 = (base + n - 1) / per;
   if (w0 == w1) return;  // finished by one worker
@@ -1288,8 +1293,8 @@ static int launch_attention_t(const AttnCall& c) {
   MLA_LAUNCH_CHECK();
   if (self) {
     dim3 cgrid((unsigned)((c.H * (c.d_c / VEC) + 255) / 256), (unsigned)c.R);
-    hipLaunchKernelGGL((self_combine_kernel<T, VEC>), cgrid, dim3(256), 0, c.stream, c.map, pl, c.H, c.d_c,
-                       (T*)c.out, c.lse);
+    hipLaunchKernelGGL((self_combine_kernel<T, VEC>), cgrid, dim3(256), 0, c.stream, pl, c.H, c.d_c, (T*)c.out,
+                       c.lse);
   } else {
     // at most min(R, G - 1) rows are cut by the G - 1 worker boundaries
     const unsigned max_split = (unsigned)(c.R < c.G ? c.R : c.G);
