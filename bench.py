@@ -1,8 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark: DeepSeek-V2-shaped absorbed-MLA decode on one MI355X.
 
-One step = the whole decode path for one batch: the planning kernel, the
-latent attention kernel, the log-sum-exp combine and the W_UV up-projection
+One step = the whole decode path for one batch, one library call: the latent
+attention kernel (which plans the batch's split over workers itself), then one
+kernel that merges the rows cut over several workers (log-sum-exp combine) and
+applies the W_UV up-projection
 (B=64 sequences x 4096 cached positions, H=128, d_c=512, d_r=64, d_v=128,
 bf16 storage, fp32 accumulation). Inputs are synthetic (seeded), resident in
 HBM before timing, and rotated over several independent copies so the
@@ -142,14 +144,15 @@ def main():
                          lse=torch.empty((B, H), dtype=torch.float32, device=dev),
                          v=torch.empty((B, H, D_V), dtype=torch.bfloat16, device=dev)))
     G_workers = M.default_workers()
-    ws = torch.empty(M.decode_workspace_bytes(B, H, D_C, G_workers), dtype=torch.uint8, device=dev)
+    ws = torch.empty(M.decode_up_v_workspace_bytes(B, H, D_C, G_workers), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
+        # one call: attention over the latent cache, then the split-row merge
+        # fused with the W_UV up-projection
         s = sets[i % len(sets)]
-        M.latent_decode(s["q"], s["cache"], lens, D_C, case.kq_scale, out=s["out"], lse=s["lse"],
-                        workspace=ws, timing_events=ev)
-        M.up_v(s["out"], wuv, out=s["v"])
+        M.latent_decode_up_v(s["q"], s["cache"], lens, D_C, case.kq_scale, wuv, out=s["v"], lse=s["lse"],
+                             workspace=ws, timing_events=ev)
 
     for i in range(args.warmup):
         step(i)
@@ -183,11 +186,16 @@ def main():
 
     # Per entry point: blocks of back-to-back calls between two events (the
     # events' own cost is spread over the block); median and min over blocks.
+    ws_two = torch.empty(M.decode_workspace_bytes(B, H, D_C, G_workers), dtype=torch.uint8, device=dev)
     entry = {
-        "latent_decode (plan + attention + combine)": time_entry(
+        "latent_decode_up_v (attention + merge fused with W_UV)": time_entry(
+            torch, stream, lambda i: M.latent_decode_up_v(sets[i % len(sets)]["q"], sets[i % len(sets)]["cache"],
+                                                          lens, D_C, case.kq_scale, wuv, out=sets[i % len(sets)]["v"],
+                                                          lse=sets[i % len(sets)]["lse"], workspace=ws)),
+        "latent_decode (attention + combine)": time_entry(
             torch, stream, lambda i: M.latent_decode(sets[i % len(sets)]["q"], sets[i % len(sets)]["cache"], lens,
                                                      D_C, case.kq_scale, out=sets[i % len(sets)]["out"],
-                                                     lse=sets[i % len(sets)]["lse"], workspace=ws)),
+                                                     lse=sets[i % len(sets)]["lse"], workspace=ws_two)),
         "up_v (W_UV stays in the last-level cache between calls)": time_entry(
             torch, stream, lambda i: M.up_v(sets[i % len(sets)]["out"], wuv, out=sets[i % len(sets)]["v"])),
     }

@@ -4,5 +4,6 @@ The computation lives in libmla.so (hand-written HIP kernels behind the C
 ABI declared in include/mla.h); this package is its Python binding.
 """
 from ._lib import (LIB_PATH, MLA_BF16, MLA_F32, MLAError, SIGNATURES, absorb_q,  # noqa: F401
-                   decode_workspace_bytes, default_workers, kq_scale_for, latent_decode,
-                   latent_prefill_causal, lib, lse_combine, prefill_workspace_bytes, up_v)
+                   decode_up_v_workspace_bytes, decode_workspace_bytes, default_workers, kq_scale_for,
+                   latent_decode, latent_decode_up_v, latent_prefill_causal, lib, lse_combine,
+                   prefill_workspace_bytes, up_v)

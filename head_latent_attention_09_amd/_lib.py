@@ -32,6 +32,9 @@ SIGNATURES = [
     ("mla_latent_decode_workspace", _sz, [_i, _i, _i, _i]),
     ("mla_latent_decode", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i,
                                _vp, _vp, _vp, _sz, _i, _vp, _vp]),
+    ("mla_latent_decode_up_v_workspace", _sz, [_i, _i, _i, _i]),
+    ("mla_latent_decode_up_v", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _i,
+                                    _vp, _vp, _vp, _sz, _i, _vp, _vp]),
     ("mla_latent_prefill_causal_workspace", _sz, [_i, _i, _i, _i, _i]),
     ("mla_latent_prefill_causal", _i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                                        _vp, _vp, _vp, _sz, _i, _vp, _vp]),
@@ -183,6 +186,45 @@ def latent_decode(q, cache, seq_lens, d_c, kq_scale, block_table=None, num_pages
     _check("mla_latent_decode", lib.mla_latent_decode(
         _ptr(q), _ptr(cache), _ptr(seq_lens), _ptr(block_table), B, H, d_c, d_r, stride, page_size,
         max_pages, num_pages, float(kq_scale), _dtype_code(q), _ptr(_dev(out, "out")), _ptr(lse),
+        _ptr(ws), ws.numel(), num_workers, None if ev is None else ev[0], _stream()))
+    return out, lse
+
+
+def decode_up_v_workspace_bytes(batch, n_heads, d_c, num_workers=0) -> int:
+    return int(lib.mla_latent_decode_up_v_workspace(batch, n_heads, d_c, num_workers))
+
+
+def latent_decode_up_v(q, cache, seq_lens, d_c, kq_scale, w_uv, block_table=None, num_pages=None, num_workers=0,
+                       out=None, lse=None, want_lse=True, workspace=None, timing_events=None):
+    """Absorbed decode and the W_UV up-projection in one call.
+
+    As latent_decode, plus w_uv [H,d_v,d_c]. Returns (v [B,H,d_v], lse [B,H] or None)."""
+    _dev(q, "q"), _dev(cache, "cache"), _dev(seq_lens, "seq_lens"), _dev(w_uv, "w_uv")
+    B, H, W = q.shape
+    d_r = W - d_c
+    d_v = w_uv.shape[1]
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    if block_table is not None:
+        _dev(block_table, "block_table")
+        if block_table.dtype != torch.int32:
+            raise TypeError("block_table must be int32")
+        page_size, max_pages = cache.shape[1], block_table.shape[1]
+        num_pages = cache.shape[0] if num_pages is None else num_pages
+        stride = 0
+    else:
+        page_size = max_pages = num_pages = 0
+        stride = cache.shape[1]
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    nb = decode_up_v_workspace_bytes(B, H, d_c, num_workers)
+    ws = _workspace(nb, q.device, workspace)
+    ev = _events(timing_events)
+    _check("mla_latent_decode_up_v", lib.mla_latent_decode_up_v(
+        _ptr(q), _ptr(cache), _ptr(seq_lens), _ptr(block_table), B, H, d_c, d_r, stride, page_size,
+        max_pages, num_pages, float(kq_scale), _ptr(w_uv), d_v, _dtype_code(q), _ptr(_dev(out, "out")), _ptr(lse),
         _ptr(ws), ws.numel(), num_workers, None if ev is None else ev[0], _stream()))
     return out, lse
 

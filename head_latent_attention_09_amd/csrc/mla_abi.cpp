@@ -119,10 +119,13 @@ static int common_attn_checks(const void* q, const void* cache, void* out, float
   return MLA_OK;
 }
 
-int mla_latent_decode(const void* q, const void* latent_cache, const int32_t* seq_lens, const int32_t* block_table,
-                      int batch, int n_heads, int d_c, int d_r, int cache_stride, int page_size, int max_pages,
-                      int num_pages, float kq_scale, int dtype, void* out_lat, float* lse, void* workspace,
-                      size_t workspace_bytes, int num_workers, void* const* timing_events, void* stream) {
+// decode, with the up-projection when w_uv is given (v then receives it and
+// out_lat is scratch inside the workspace)
+static int decode_call(const void* q, const void* latent_cache, const int32_t* seq_lens, const int32_t* block_table,
+                       int batch, int n_heads, int d_c, int d_r, int cache_stride, int page_size, int max_pages,
+                       int num_pages, float kq_scale, int dtype, void* out_lat, float* lse, void* workspace,
+                       size_t workspace_bytes, int num_workers, void* const* timing_events, void* stream,
+                       const void* w_uv, int d_v, void* v) {
   int st = attn_dims_check(batch, n_heads, d_c, d_r);
   if (st != MLA_OK) return st;
   if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
@@ -146,7 +149,12 @@ int mla_latent_decode(const void* q, const void* latent_cache, const int32_t* se
   const int G = resolve_workers(num_workers);
   if (G <= 0) return G == 0 ? MLA_ERR_SHAPE : G;
   if (!workspace) return MLA_ERR_WORKSPACE;
-  if (workspace_bytes < plan_bytes(batch, G, n_heads, d_c)) return MLA_ERR_WORKSPACE;
+  size_t need = plan_bytes(batch, G, n_heads, d_c);
+  if (w_uv) {  // out_lat in the workspace, after the plan
+    out_lat = (char*)workspace + need;
+    need += align256((size_t)batch * n_heads * d_c * sizeof(float));
+  }
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
 
   AttnCall c{};
   c.q = q;
@@ -170,7 +178,42 @@ int mla_latent_decode(const void* q, const void* latent_cache, const int32_t* se
   c.G = G;
   c.timing_events = timing_events;
   c.stream = (hipStream_t)stream;
+  c.w_uv = w_uv;
+  c.v = v;
+  c.d_v = d_v;
   return launch_attention(c);
+}
+
+int mla_latent_decode(const void* q, const void* latent_cache, const int32_t* seq_lens, const int32_t* block_table,
+                      int batch, int n_heads, int d_c, int d_r, int cache_stride, int page_size, int max_pages,
+                      int num_pages, float kq_scale, int dtype, void* out_lat, float* lse, void* workspace,
+                      size_t workspace_bytes, int num_workers, void* const* timing_events, void* stream) {
+  return decode_call(q, latent_cache, seq_lens, block_table, batch, n_heads, d_c, d_r, cache_stride, page_size,
+                     max_pages, num_pages, kq_scale, dtype, out_lat, lse, workspace, workspace_bytes, num_workers,
+                     timing_events, stream, nullptr, 0, nullptr);
+}
+
+size_t mla_latent_decode_up_v_workspace(int batch, int n_heads, int d_c, int num_workers) {
+  const size_t b = mla_latent_decode_workspace(batch, n_heads, d_c, num_workers);
+  return b == 0 ? 0 : b + align256((size_t)batch * n_heads * d_c * sizeof(float));
+}
+
+int mla_latent_decode_up_v(const void* q, const void* latent_cache, const int32_t* seq_lens,
+                           const int32_t* block_table, int batch, int n_heads, int d_c, int d_r, int cache_stride,
+                           int page_size, int max_pages, int num_pages, float kq_scale, const void* w_uv, int d_v,
+                           int dtype, void* out, float* lse, void* workspace, size_t workspace_bytes, int num_workers,
+                           void* const* timing_events, void* stream) {
+  if (d_v <= 0) return MLA_ERR_SHAPE;
+  if (d_v > 4096) return MLA_ERR_UNSUPPORTED;
+  if (batch > 0) {
+    if (!w_uv || !out) return MLA_ERR_NULL;
+    const int es = (dtype == MLA_BF16) ? 2 : 4;
+    if (((uintptr_t)w_uv % es) || ((uintptr_t)out % es)) return MLA_ERR_ALIGN;
+  }
+  // out_lat is scratch in the workspace (out stands in for it in the argument checks)
+  return decode_call(q, latent_cache, seq_lens, block_table, batch, n_heads, d_c, d_r, cache_stride, page_size,
+                     max_pages, num_pages, kq_scale, dtype, out, lse, workspace, workspace_bytes, num_workers,
+                     timing_events, stream, w_uv, d_v, out);
 }
 
 int mla_latent_prefill_causal(const void* q, const void* latent_cache, int batch, int s_q, int s_kv, int n_heads,

@@ -182,6 +182,11 @@ struct AttnCall {
   int G;
   void* const* timing_events;
   hipStream_t stream;
+  // optional up-projection of the result (decode): v[r, h] = W_UV[h] out[r, h];
+  // out is then scratch for rows finished by one worker
+  const void* w_uv = nullptr;  // [H, d_v, d_c]
+  void* v = nullptr;           // [R, H, d_v]
+  int d_v = 0;
 };
 
 int attn_tile_size(const AttnCall& c);          // tile used by the kernel path chosen for c

@@ -140,6 +140,31 @@ int mla_latent_decode(const void* q, const void* latent_cache,
                       int num_workers, void* const* timing_events, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Absorbed decode followed by the value up-projection, in one call (ferrox-
+ * core module documentation: v[h] = wv_b[h] . out_lat[h]; the chain
+ * mla_latent_decode -> mla_up_v without storing out_lat):
+ *   out [batch, n_heads, d_v] = W_UV[h] out_lat[b, h] for every (b, h), with
+ *   out_lat the result mla_latent_decode computes (rounded to dtype first);
+ *   w_uv [n_heads, d_v, d_c] as in mla_up_v; lse as in mla_latent_decode.
+ * All other arguments as mla_latent_decode. workspace: at least
+ *   mla_latent_decode_up_v_workspace(batch, n_heads, d_c, num_workers)
+ *   bytes (the decode workspace plus room for out_lat). With bf16, d_c = 512
+ *   and d_v = 128 the merge of split rows and the up-projection run as one
+ *   kernel; otherwise the call runs decode, combine and up-projection.
+ * Limits: as mla_latent_decode and mla_up_v (d_v <= 4096).
+ * ------------------------------------------------------------------------- */
+size_t mla_latent_decode_up_v_workspace(int batch, int n_heads, int d_c, int num_workers);
+
+int mla_latent_decode_up_v(const void* q, const void* latent_cache,
+                           const int32_t* seq_lens, const int32_t* block_table,
+                           int batch, int n_heads, int d_c, int d_r,
+                           int cache_stride, int page_size, int max_pages, int num_pages,
+                           float kq_scale, const void* w_uv, int d_v, int dtype,
+                           void* out, float* lse,
+                           void* workspace, size_t workspace_bytes,
+                           int num_workers, void* const* timing_events, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Causal prefill over the latent cache: every query of a chunk attends to
  * the cache positions the causal mask leaves visible (gated-MLA statement:
  * later positions are masked before the softmax, diagonal included;

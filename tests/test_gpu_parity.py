@@ -108,6 +108,78 @@ def test_decode_timing_events(dtype):
     assert ev[0].elapsed_time(ev[1]) > 0
 
 
+def run_decode_up_v(case, num_workers=0):
+    q = to_dev(case.q, case.dtype)
+    lens = torch.from_numpy(case.lens.astype(np.int32)).cuda()
+    w = to_dev(case.w_uv, case.dtype)
+    if case.page_size is None:
+        v, lse = M.latent_decode_up_v(q, to_dev(case.cache, case.dtype), lens, case.d_c, case.kq_scale, w,
+                                      num_workers=num_workers)
+    else:
+        v, lse = M.latent_decode_up_v(q, to_dev(case.pages, case.dtype), lens, case.d_c, case.kq_scale, w,
+                                      block_table=torch.from_numpy(case.block_table).cuda(), num_workers=num_workers)
+    torch.cuda.synchronize()
+    return to_host64(v), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype,H,d_v,lens,paged,workers", [
+    (G.BF16, 128, 128, [700, 33, 1000], False, 7),      # merge fused with the up-projection, cut rows
+    (G.BF16, 128, 128, [1, 0, 300, 65, 0], False, 0),   # empty and one-position rows
+    (G.BF16, 64, 128, [130, 500, 64], True, 5),         # paged, 64 heads
+    (G.BF16, 128, 64, [200, 40], False, 3),             # d_v outside the fused kernel: decode, combine, up_v
+    (G.F32, 16, 24, [50, 7, 0], False, 4),              # fp32: the generic kernels
+])
+def test_decode_up_v(dtype, H, d_v, lens, paged, workers):
+    case = G.decode_case(len(lens), H, 512, 64, lens, dtype, seed=120 + H + d_v, d_v=d_v,
+                         page_size=64 if paged else None)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    say(f"decode + up_v: dtype={dtype} H={H} d_v={d_v} lens={lens} paged={paged} workers={workers}")
+    got, glse = run_decode_up_v(case, workers)
+    lat, rlse = oracle_decode(case)
+    ref = O.up_project(lat, G.to_f64(case.w_uv, dtype))
+    e, le = rel_err(got, ref), lse_err(glse, rlse)
+    say(f"  v rel err {e:.3e}  lse abs err {le:.3e}")
+    assert e <= TOL[dtype] and le <= LSE_TOL[dtype]
+    # the same as the two calls it replaces, up to the rounding of the merge
+    lat_gpu, _ = run_decode(case, workers)
+    two = O.up_project(lat_gpu, G.to_f64(case.w_uv, dtype))
+    assert rel_err(got, two) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("workers", [4, 1])
+def test_decode_up_v_large_logits(workers):
+    """The recompute path of overflowing rows under the fused merge."""
+    case = G.decode_case(2, 128, 512, 64, [600, 300], G.BF16, seed=13, d_v=128)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    cache = G.to_f64(case.cache, G.BF16)
+    cache[:, :, 512] = np.linspace(0.0, 60.0, cache.shape[1])[None, :]
+    case.cache = G.storage(cache, G.BF16)
+    q = G.to_f64(case.q, G.BF16)
+    q[:, :, 512] = 40.0
+    case.q = G.storage(q, G.BF16)
+    got, glse = run_decode_up_v(case, workers)
+    lat, rlse = oracle_decode(case)
+    ref = O.up_project(lat, G.to_f64(case.w_uv, G.BF16))
+    assert rel_err(got, ref) <= TOL[G.BF16] and lse_err(glse, rlse) <= LSE_TOL[G.BF16]
+
+
+@pytest.mark.parametrize("rows,workers", [(300, 0), (1, 200)])
+def test_decode_up_v_plan_kernel_and_many_parts(rows, workers):
+    """The fused merge after the planning kernel (more than 256 rows), and a
+    row cut into about 190 parts."""
+    if rows == 1:
+        case = G.decode_case(1, 128, 512, 64, [3000], G.BF16, seed=42, d_v=128)
+    else:
+        lens = np.random.default_rng(6).integers(0, 41, rows)
+        case = G.decode_case(rows, 32, 512, 64, lens, G.BF16, seed=56, d_v=128)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    say(f"decode + up_v: rows={rows} workers={workers}")
+    got, glse = run_decode_up_v(case, workers)
+    lat, rlse = oracle_decode(case)
+    ref = O.up_project(lat, G.to_f64(case.w_uv, G.BF16))
+    assert rel_err(got, ref) <= TOL[G.BF16] and lse_err(glse, rlse) <= LSE_TOL[G.BF16]
+
+
 def test_decode_batch_planned_by_kernel():
     """More rows than the attention kernel plans for itself (256): the MFMA
     kernel then reads the planning kernel's results."""
