@@ -14,7 +14,7 @@ Prints ONE JSON line. `value` is latent head-tokens attended per second
 (B*H*seq per step). `roofline` is for the dominant kernel (the latent
 attention kernel), timed with two HIP events passed with its launch on its own
 stream (they take the start and end of its dispatch) on every n-th timed step
-(--event-every, default 5: an evented launch adds about 5 us of stream time).
+(--event-every, default 5).
 `entry_points_ms` gives each entry point's own time (median and min over
 blocks of back-to-back calls). `cpu_baseline` times the fp64 CPU oracle on a
 bounded sample of the same workload on this host.
@@ -50,8 +50,10 @@ ESIZE = 2
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # about 200 steps (25 ms) pass before the GPU's clocks settle after idle;
+    # fewer warm-up steps time part of that ramp
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--copies", type=int, default=3, help="rotated input copies")
     p.add_argument("--event-every", type=int, default=5,
                    help="record the attention kernel's timing events on every n-th timed step")
@@ -158,11 +160,10 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # An evented launch adds about 5 us of stream time, so the attention
-    # kernel is timed on every n-th step of the timed region rather than on
-    # every step. The dispatch start is taken when the dispatch is picked up,
-    # which can be while the planning kernel before it still runs (a few us
-    # of it fall inside the interval: the measured rate is a lower bound).
+    # The attention kernel is timed on every n-th step of the timed region.
+    # The dispatch start is taken when the dispatch is picked up, which can be
+    # while the kernel before it still drains (a few us of it fall inside the
+    # interval: the measured rate is a lower bound).
     every = max(1, args.event_every)
     attn_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(0, args.steps, every)]

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["mla_abi.cpp", "mla_attn.hip", "mla_gemm.hip"]
+SOURCES = ["mla_abi.cpp", "mla_attn.hip", "mla_decode_upv.hip", "mla_gemm.hip"]
 ARCH = "gfx950"
 
 

@@ -1192,240 +1192,6 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(const float* o_parts, 
   combine_head<OutT>(n, part, d_c, out + ((size_t)r * H + h) * d_c, lse ? lse + (size_t)r * H + h : nullptr);
 }
 
-// ===========================================================================
-// decode: split-row merge fused with the W_UV up-projection
-// ===========================================================================
-// Workgroup (row block, head): A = the 32 rows' latent outputs of head h,
-// built in LDS from the attention kernel's results -- a row one worker
-// finished (or recomputed) is read from `lat`, a cut row is merged from its
-// partial outputs (the combine's merge), an empty row is zero -- then
-// v[rows, h, :] = A W_UV[h]^T with 32x32x16 bf16 MFMA. Saves the combine
-// kernel and the round trip of the merged rows through HBM.
-//
-// Eight waves in two roles, so that neither role's loads queue behind the
-// other's (a wave's loads complete in issue order): waves 0-3 build A (row
-// information with eight lanes per row, then the rows' partial outputs, two
-// rows and four parts per batch of loads); waves 4-7 stream W_UV[h] through
-// LDS in 64-wide K slices (three in flight) and own the MFMA, one 32-column
-// block of v each.
-namespace fu {
-constexpr int FR = 32;                        // rows per workgroup
-constexpr int FK = 512;                       // d_c
-constexpr int FV = 128;                       // d_v (one 32-column block per MFMA wave)
-constexpr int FSL = 64;                       // K slice
-constexpr int FNB = 4;                        // W slice buffers
-constexpr int NSL = FK / FSL;                 // 8 slices
-constexpr int FPW = 8;                        // part weights kept per row (more parts: weights from HBM)
-constexpr int A_ROW = FK * 2;                 // 1 KiB per A row
-constexpr int W_SLICE = FV * FSL * 2;         // 16 KiB
-constexpr int LDS_W = FR * A_ROW;             // A tile first (32 KiB), then the W ring
-constexpr int FSMEM = LDS_W + FNB * W_SLICE;  // 96 KiB
-
-// A row r, 16-byte chunk c at chunk c ^ (r & 7) (MFMA operand reads of 32 rows spread over the banks)
-__device__ __forceinline__ int a_off(int r, int c) { return r * A_ROW + ((c ^ (r & 7)) << 4); }
-// W slice: column j (128 B of K) chunk c at chunk c ^ (j & 7)
-__device__ __forceinline__ int w_off(int j, int c) { return j * (FSL * 2) + ((c ^ (j & 7)) << 4); }
-
-// a pointer the compiler keeps in vector registers, made an SGPR operand (its value is the same in every lane)
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  const uint64_t u = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ void fdma16(const void* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(gbase), "s"(lds) : "memory");
-}
-// wait until at most n (a multiple of 4, 0..12) of this wave's loads are in flight
-__device__ __forceinline__ void wait_w(int n) {
-  if (n >= 12) __builtin_amdgcn_s_waitcnt(12 | (7 << 4) | (15 << 8));
-  else if (n >= 8) __builtin_amdgcn_s_waitcnt(8 | (7 << 4) | (15 << 8));
-  else if (n >= 4) __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8));
-  else __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-}
-
-__global__ __launch_bounds__(512, 1) void upv_merge_kernel(Plan pl, int H, const bf16* lat, const bf16* w_uv,
-                                                           bf16* v, float* lse) {
-  __shared__ __attribute__((aligned(1024))) char smem[FSMEM];
-  __shared__ int rk[FR], rs0[FR], rw0[FR], rn[FR];  // row kind (0 empty, 1 read, 2 merge), its parts
-  __shared__ float rl[FR], rwt[FR][FPW];             // merged lse of a cut row, its parts' weights
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = __builtin_amdgcn_readfirstlane(blockIdx.x % H);  // the division runs on the vector ALUs
-  const int n0 = __builtin_amdgcn_readfirstlane((blockIdx.x / H) * FR);
-  const int R = pl.R;
-  const bool mw = wv >= 4;  // MFMA / W wave
-  const int mwv = wv - 4;
-
-  // W_UV[h] slice sl: column j = 0..127, K 64 sl .. 64 sl + 63: 16 loads of 1 KiB, 4 per MFMA wave
-  auto issue_w = [&](int sl) {
-    char* buf = smem + LDS_W + (sl % FNB) * W_SLICE;
-    const void* gb = uniform_ptr(w_uv + (size_t)h * FV * FK + sl * FSL);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ld = mwv * 4 + i;
-      const int p = ld * 64 + lane;
-      const int j = p >> 3, c = p & 7;
-      const int cs = c ^ (j & 7);  // this lane's LDS slot holds global chunk cs
-      fdma16(gb, (uint32_t)((j * FK + cs * 8) * 2), (uint32_t)(uintptr_t)(const MLA_LDS char*)(buf + ld * 1024));
-    }
-  };
-  if (mw) {
-#pragma unroll
-    for (int sl = 0; sl < FNB; ++sl) issue_w(sl);
-  } else {
-    // row information: eight lanes per row, lane k reads the lse of parts k, k + 8, ...
-    const int row = tid >> 3, k = tid & 7, r = n0 + row;
-    int kind = 0, s0 = 0, w0 = 0, np = 0;
-    float mx = -INFINITY, ws = 0.f, l_first = -INFINITY;
-    bool marked = false;
-    if (r < R && pl.len[r] > 0) {
-      const int base = pl.cum[r], n = pl.cum[r + 1] - base, total = pl.cum[R], c = pl.split[1];
-      const int per = plan_per_worker(total, pl.G);
-      const int sf = base + c;
-      w0 = sf / per;
-      const int w1 = (base + n - 1) / per;
-      kind = 1;
-      if (w0 != w1) {
-        np = w1 - w0 + 1;
-        s0 = plan_slot(w0, sf, per);
-        for (int i = k; i < np; i += FPW) {
-          const float l = pl.part_lse[(size_t)(i == 0 ? s0 : 2 * (w0 + i)) * H + h];
-          if (i == k) l_first = l;
-          marked |= l != l;
-          if (l > mx) {
-            ws = ws * __expf(mx - l) + 1.f;
-            mx = l;
-          } else if (l != -INFINITY) {
-            ws += __expf(l - mx);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int off = 1; off < FPW; off <<= 1) {
-      const float om = __shfl_xor(mx, off), ow = __shfl_xor(ws, off);
-      marked |= __shfl_xor((int)marked, off) != 0;
-      const float m2 = fmaxf(mx, om);
-      ws = (mx == -INFINITY ? 0.f : ws * __expf(mx - m2)) + (om == -INFINITY ? 0.f : ow * __expf(om - m2));
-      mx = m2;
-    }
-    float l_tot = -INFINITY;
-    if (kind == 1 && np > 0 && !marked) {  // a marked row was recomputed into `lat`
-      kind = 2;
-      l_tot = ws > 0.f ? mx + __logf(ws) : -INFINITY;
-    }
-    if (k < np) rwt[row][k] = (l_first == -INFINITY || l_tot == -INFINITY) ? 0.f : __expf(l_first - l_tot);
-    if (k == 0) {
-      rk[row] = kind;
-      rs0[row] = s0;
-      rw0[row] = w0;
-      rn[row] = np;
-      rl[row] = l_tot;
-      if (r < R && lse && kind != 1) lse[(size_t)r * H + h] = l_tot;  // empty rows -inf, cut rows merged
-    }
-  }
-  __syncthreads();
-
-  if (!mw) {
-    // A tile: wave wv builds rows 8 wv .. 8 wv + 7, lane = 16-byte chunk; two rows and four sources per batch
-    const bf16* po = (const bf16*)pl.part_o;
-    auto nsrc = [&](int row) { return rk[row] == 0 ? 0 : rk[row] == 1 ? 1 : rn[row]; };
-    auto src = [&](int row, int i) -> const bf16* {
-      if (rk[row] == 1) return lat + ((size_t)(n0 + row) * H + h) * FK;
-      const int slot = i == 0 ? rs0[row] : 2 * (rw0[row] + i);
-      return po + ((size_t)slot * H + h) * FK;
-    };
-    auto weight = [&](int row, int i) -> float {
-      if (rk[row] == 1) return 1.f;
-      if (i < FPW) return rwt[row][i];
-      const float l = pl.part_lse[(size_t)(2 * (rw0[row] + i)) * H + h];
-      return l == -INFINITY ? 0.f : __expf(l - rl[row]);
-    };
-    for (int rr = 0; rr < 8; rr += 2) {
-      const int ra = wv * 8 + rr, rb = ra + 1;
-      const int na = __builtin_amdgcn_readfirstlane(nsrc(ra)), nb = __builtin_amdgcn_readfirstlane(nsrc(rb));
-      const int nmax = na > nb ? na : nb;
-      float acc_a[8], acc_b[8];
-#pragma unroll
-      for (int x = 0; x < 8; ++x) acc_a[x] = acc_b[x] = 0.f;
-      for (int p0 = 0; p0 < nmax; p0 += 4) {
-        bf16x8 va[4], vb[4];
-        float wa[4], wb[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          wa[j] = wb[j] = 0.f;
-          if (p0 + j < na) va[j] = *(const bf16x8*)(src(ra, p0 + j) + lane * 8);
-          if (p0 + j < nb) vb[j] = *(const bf16x8*)(src(rb, p0 + j) + lane * 8);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (p0 + j < na) {
-            wa[j] = weight(ra, p0 + j);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) acc_a[x] += wa[j] * (float)va[j][x];
-          }
-          if (p0 + j < nb) {
-            wb[j] = weight(rb, p0 + j);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) acc_b[x] += wb[j] * (float)vb[j][x];
-          }
-        }
-      }
-      bf16x8 oa, ob;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        oa[x] = f32_to_bf16(acc_a[x]);
-        ob[x] = f32_to_bf16(acc_b[x]);
-      }
-      *(MLA_LDS bf16x8*)(smem + a_off(ra, lane)) = oa;
-      *(MLA_LDS bf16x8*)(smem + a_off(rb, lane)) = ob;
-    }
-  }
-
-  // v^T block: MFMA wave mwv owns columns 32 mwv .. 32 mwv + 31 of all 32 rows. Slice sl is
-  // waited for, then one barrier: slice sl and the A tile are in LDS, and every wave is done
-  // with slice sl - 1, whose buffer then takes slice sl + 3.
-  f32x16 acc = f32x16{};
-  const int g = lane >> 5;
-  for (int sl = 0; sl < NSL; ++sl) {
-    if (mw) {
-      const int last = sl == 0 ? FNB - 1 : (sl + FNB - 2 < NSL - 1 ? sl + FNB - 2 : NSL - 1);  // last slice issued
-      wait_w(4 * (last - sl));
-    }
-    __syncthreads();
-    if (mw) {
-      if (sl >= 1 && sl + FNB - 1 < NSL) issue_w(sl + FNB - 1);
-      const char* wb = smem + LDS_W + (sl % FNB) * W_SLICE;
-#pragma unroll
-      for (int ks = 0; ks < FSL / 16; ++ks) {
-        const int row = lane & 31, kc = sl * (FSL / 8) + 2 * ks + g;  // A: row, K chunk (of 64)
-        const bf16x8 af = *(const MLA_LDS bf16x8*)(smem + a_off(row, kc));
-        const int j = mwv * 32 + (lane & 31), wc = 2 * ks + g;      // W: column, K chunk of the slice
-        const bf16x8 bw = *(const MLA_LDS bf16x8*)(wb + w_off(j, wc));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bw, acc, 0, 0, 0);
-      }
-    }
-  }
-  __syncthreads();  // every MFMA wave is done with the A tile
-
-  // output: stage the 32 x 128 block in the A tile, store whole 256-byte rows
-  // (D layout: column lane % 32, rows 8 (q / 4) + 4 g + q % 4)
-  if (mw) {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = 8 * (q >> 2) + 4 * g + (q & 3);
-      *(MLA_LDS bf16*)(smem + row * 256 + (mwv * 32 + (lane & 31)) * 2) = f32_to_bf16(acc[q]);
-    }
-  }
-  __syncthreads();
-  {
-    const int row = tid >> 4, c = tid & 15;
-    const int r = n0 + row;
-    if (r < R) *(bf16x8*)(v + ((size_t)r * H + h) * FV + c * 8) = *(const MLA_LDS bf16x8*)(smem + row * 256 + c * 16);
-  }
-}
-}  // namespace fu
 
 // ===========================================================================
 // host launchers
@@ -1527,14 +1293,8 @@ static int launch_attention_t(const AttnCall& c) {
   }
   MLA_LAUNCH_CHECK();
   // decode with the up-projection: merge and W_UV in one kernel (bf16, d_c = 512, d_v = 128)
-  if (c.w_uv && mfma && c.map.mode != 2 && c.d_v == fu::FV && c.d_c == fu::FK && aligned16(c.w_uv) &&
-      aligned16(c.v)) {
-    const unsigned blocks = (unsigned)(((int64_t)c.R + fu::FR - 1) / fu::FR * c.H);
-    hipLaunchKernelGGL(fu::upv_merge_kernel, dim3(blocks), dim3(512), 0, c.stream, pl, c.H, (const bf16*)c.out,
-                       (const bf16*)c.w_uv, (bf16*)c.v, c.lse);
-    MLA_LAUNCH_CHECK();
-    return MLA_OK;
-  }
+  if (c.w_uv && mfma && c.map.mode != 2 && upv_merge_fits(c.d_c, c.d_v, c.w_uv, c.v))
+    return launch_upv_merge(pl, c.R, c.H, c.out, c.w_uv, c.v, c.lse, c.stream);
   if (self) {
     dim3 cgrid((unsigned)((c.H * (c.d_c / VEC) + 255) / 256), (unsigned)c.R);
     hipLaunchKernelGGL((self_combine_kernel<T, VEC>), cgrid, dim3(256), 0, c.stream, pl, c.H, c.d_c, (T*)c.out,

@@ -197,5 +197,10 @@ int launch_absorb(const void* q_nope, const void* q_pe, const void* w_uk, void* 
                   int H, int d_nope, int d_c, int d_r, int dtype, hipStream_t stream);
 int launch_up_v(const void* lat, const void* w_uv, void* out, int64_t N, int H, int d_c,
                 int d_v, int dtype, hipStream_t stream);
+// decode rows' merge fused with the up-projection: lat = the attention kernel's
+// outputs of rows finished by one worker, pl = its plan (bf16, d_c = 512, d_v = 128)
+bool upv_merge_fits(int d_c, int d_v, const void* w_uv, const void* v);
+int launch_upv_merge(const Plan& pl, int R, int H, const void* lat, const void* w_uv, void* v, float* lse,
+                     hipStream_t stream);
 
 }  // namespace mla
