@@ -19,8 +19,8 @@ namespace mla {
 //
 // Eight waves in two roles, so that neither role's loads queue behind the
 // other's (a wave's loads complete in issue order): waves 0-3 build A (row
-// information with eight lanes per row, then the rows' partial outputs, two
-// rows and four parts per batch of loads); waves 4-7 stream W_UV[h] through
+// information with eight lanes per row, then the rows' partial outputs, four
+// rows and up to eight parts each per batch of loads); waves 4-7 stream W_UV[h] through
 // a ring of four 64-wide K slices in LDS and own the MFMA, one 32-column
 // block of v each.
 namespace fu {
@@ -94,8 +94,11 @@ __global__ __launch_bounds__(512, 1) void upv_merge_kernel(Plan pl, int H, const
     int kind = 0, s0 = 0, w0 = 0, np = 0;
     float mx = -INFINITY, ws = 0.f, l_first = -INFINITY;
     bool marked = false;
-    if (r < R && pl.len[r] > 0) {
-      const int base = pl.cum[r], n = pl.cum[r + 1] - base, total = pl.cum[R], c = pl.split[1];
+    // every plan entry in one round of loads (rows past the batch read the last row's)
+    const int rc = r < R ? r : R - 1;
+    const int len = pl.len[rc], base = pl.cum[rc], n = pl.cum[rc + 1] - base, total = pl.cum[R], c = pl.split[1];
+    asm volatile("" ::"v"(len), "v"(base), "v"(n), "s"(total), "s"(c));  // keeps the loads ahead of the branch on len
+    if (r < R && len > 0) {
       const int per = plan_per_worker(total, pl.G);
       const int sf = base + c;
       w0 = sf / per;
@@ -143,58 +146,68 @@ __global__ __launch_bounds__(512, 1) void upv_merge_kernel(Plan pl, int H, const
   __syncthreads();
 
   if (!mw) {
-    // A tile: wave wv builds rows 8 wv .. 8 wv + 7, lane = 16-byte chunk; two rows and four sources per batch
+    // A tile: wave wv builds rows 8 wv .. 8 wv + 7, lane = 16-byte chunk. Per batch of four
+    // rows: their plan entries into scalar registers first, then the loads of up to eight
+    // sources per row back to back (into zeroed registers, so that no skipped load leaves a
+    // register the compiler could reuse while another load is in flight), then the sums.
     const bf16* po = (const bf16*)pl.part_o;
-    auto nsrc = [&](int row) { return rk[row] == 0 ? 0 : rk[row] == 1 ? 1 : rn[row]; };
-    auto src = [&](int row, int i) -> const bf16* {
-      if (rk[row] == 1) return lat + ((size_t)(n0 + row) * H + h) * FK;
-      const int slot = i == 0 ? rs0[row] : 2 * (rw0[row] + i);
-      return po + ((size_t)slot * H + h) * FK;
-    };
-    auto weight = [&](int row, int i) -> float {
-      if (rk[row] == 1) return 1.f;
-      if (i < FPW) return rwt[row][i];
-      const float l = pl.part_lse[(size_t)(2 * (rw0[row] + i)) * H + h];
-      return l == -INFINITY ? 0.f : __expf(l - rl[row]);
-    };
-    for (int rr = 0; rr < 8; rr += 2) {
-      const int ra = wv * 8 + rr, rb = ra + 1;
-      const int na = __builtin_amdgcn_readfirstlane(nsrc(ra)), nb = __builtin_amdgcn_readfirstlane(nsrc(rb));
-      const int nmax = na > nb ? na : nb;
-      float acc_a[8], acc_b[8];
+    constexpr int RB = 4;
 #pragma unroll
-      for (int x = 0; x < 8; ++x) acc_a[x] = acc_b[x] = 0.f;
-      for (int p0 = 0; p0 < nmax; p0 += 4) {
-        bf16x8 va[4], vb[4];
-        float wa[4], wb[4];
+    for (int rr = 0; rr < 8; rr += RB) {
+      int kind[RB], s0[RB], w0[RB], n[RB];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          wa[j] = wb[j] = 0.f;
-          if (p0 + j < na) va[j] = *(const bf16x8*)(src(ra, p0 + j) + lane * 8);
-          if (p0 + j < nb) vb[j] = *(const bf16x8*)(src(rb, p0 + j) + lane * 8);
+      for (int i = 0; i < RB; ++i) {
+        const int row = wv * 8 + rr + i;
+        kind[i] = __builtin_amdgcn_readfirstlane(rk[row]);
+        s0[i] = __builtin_amdgcn_readfirstlane(rs0[row]);
+        w0[i] = __builtin_amdgcn_readfirstlane(rw0[row]);
+        n[i] = kind[i] == 0 ? 0 : kind[i] == 1 ? 1 : __builtin_amdgcn_readfirstlane(rn[row]);
+      }
+      auto src = [&](int i, int j) -> const bf16* {
+        if (kind[i] == 1) return lat + ((size_t)(n0 + wv * 8 + rr + i) * H + h) * FK;
+        return po + ((size_t)(j == 0 ? s0[i] : 2 * (w0[i] + j)) * H + h) * FK;
+      };
+      bf16x8 pv[RB][FPW];
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < FPW; ++j)
+#pragma unroll
+          for (int x = 0; x < 8; ++x) pv[i][j][x] = (bf16)0.f;
+#pragma unroll
+      for (int j = 0; j < FPW; ++j)
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+          if (j < n[i]) pv[i][j] = *(const bf16x8*)(src(i, j) + lane * 8);
+      float acc[RB][8];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int row = wv * 8 + rr + i;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[i][x] = 0.f;
+#pragma unroll
+        for (int j = 0; j < FPW; ++j) {
+          const float w = j >= n[i] ? 0.f : kind[i] == 1 ? 1.f : rwt[row][j];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) acc[i][x] += w * (float)pv[i][j][x];
         }
+        // parts beyond the first eight (rows cut over many workers): one at a time,
+        // weights from their lse in HBM
+        for (int j = FPW; j < n[i]; ++j) {
+          const float l = pl.part_lse[(size_t)(2 * (w0[i] + j)) * H + h];
+          const float w = l == -INFINITY ? 0.f : __expf(l - rl[row]);
+          const bf16x8 v = *(const bf16x8*)(src(i, j) + lane * 8);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (p0 + j < na) {
-            wa[j] = weight(ra, p0 + j);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) acc_a[x] += wa[j] * (float)va[j][x];
-          }
-          if (p0 + j < nb) {
-            wb[j] = weight(rb, p0 + j);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) acc_b[x] += wb[j] * (float)vb[j][x];
-          }
+          for (int x = 0; x < 8; ++x) acc[i][x] += w * (float)v[x];
         }
       }
-      bf16x8 oa, ob;
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        oa[x] = f32_to_bf16(acc_a[x]);
-        ob[x] = f32_to_bf16(acc_b[x]);
+      for (int i = 0; i < RB; ++i) {
+        bf16x8 o;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) o[x] = f32_to_bf16(acc[i][x]);
+        *(MLA_LDS bf16x8*)(smem + a_off(wv * 8 + rr + i, lane)) = o;
       }
-      *(MLA_LDS bf16x8*)(smem + a_off(ra, lane)) = oa;
-      *(MLA_LDS bf16x8*)(smem + a_off(rb, lane)) = ob;
     }
   }
 
