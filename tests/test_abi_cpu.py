@@ -102,6 +102,36 @@ def test_decode_validation():
     assert _decode(B=0, dtype=5) == -3 and _decode(B=0, scale=math.nan) == -7 and _decode(B=0, H=0) == -2
 
 
+def _decode_up_v(**kw):
+    a = dict(q=FAKE, cache=FAKE, lens=FAKE, table=None, B=2, H=4, d_c=16, d_r=4, stride=8, page=0,
+             max_pages=0, num_pages=0, scale=0.3, w=FAKE, d_v=8, dtype=M.MLA_F32, out=FAKE, lse=FAKE, ws=FAKE,
+             ws_bytes=1 << 30, workers=8)
+    a.update(kw)
+    return M.lib.mla_latent_decode_up_v(a["q"], a["cache"], a["lens"], a["table"], a["B"], a["H"], a["d_c"],
+                                        a["d_r"], a["stride"], a["page"], a["max_pages"], a["num_pages"],
+                                        a["scale"], a["w"], a["d_v"], a["dtype"], a["out"], a["lse"], a["ws"],
+                                        a["ws_bytes"], a["workers"], None, None)
+
+
+def test_decode_up_v_validation():
+    """The decode checks plus W_UV's: every failure returns before any launch."""
+    assert _decode_up_v(d_v=0) == -2 and _decode_up_v(d_v=-4) == -2
+    assert _decode_up_v(d_v=4097) == -4
+    assert _decode_up_v(w=None) == -1 and _decode_up_v(out=None) == -1 and _decode_up_v(lens=None) == -1
+    assert _decode_up_v(w=FAKE + 2) == -6 and _decode_up_v(out=FAKE + 2) == -6
+    assert _decode_up_v(dtype=2) == -3 and _decode_up_v(scale=math.nan) == -7
+    assert _decode_up_v(H=0) == -2 and _decode_up_v(d_c=2048) == -4
+    assert _decode_up_v(ws=None) == -5
+    # the latent rows live in the workspace: the two-call workspace is too small
+    need = M.decode_up_v_workspace_bytes(2, 4, 16, 8)
+    assert need == M.decode_workspace_bytes(2, 4, 16, 8) + (2 * 4 * 16 * 4 + 255) // 256 * 256
+    assert _decode_up_v(ws_bytes=need - 1) == -5
+    assert _decode_up_v(ws_bytes=M.decode_workspace_bytes(2, 4, 16, 8)) == -5
+    assert _decode_up_v(B=0) == 0
+    assert _decode_up_v(B=0, q=None, cache=None, lens=None, w=None, out=None, lse=None, ws=None) == 0
+    assert _decode_up_v(B=0, d_v=0) == -2
+
+
 def test_prefill_validation():
     def call(**kw):
         a = dict(q=FAKE, cache=FAKE, B=1, S_q=4, S_kv=4, H=2, d_c=16, d_r=4, scale=0.2,
