@@ -316,8 +316,13 @@ def test_config3_sampled():
     w_uv = to_dev(case.w_uv, G.BF16)
     out_lat, lse = M.latent_decode(q, cache, lens, 512, case.kq_scale)
     v = M.up_v(out_lat, w_uv)
+    # the benchmark's call: attention, then the merge fused with the up-projection
+    vf, lsef = M.latent_decode_up_v(q, cache, lens, 512, case.kq_scale, w_uv)
     torch.cuda.synchronize()
     out_lat, v, lse = to_host64(out_lat), to_host64(v), lse.cpu().numpy()
+    vf, lsef = to_host64(vf), lsef.cpu().numpy()
+    say(f"  fused vs two calls: v {rel_err(vf, v):.2e}  lse {np.max(np.abs(lsef - lse)):.2e}")
+    assert rel_err(vf, v) <= 1e-2 and np.max(np.abs(lsef - lse)) <= 1e-4
     rng = np.random.default_rng(3)
     samples = [(0, 0), (63, 127)] + [tuple(x) for x in zip(rng.integers(0, 64, 6), rng.integers(0, 128, 6))]
     wuv = G.to_f64(case.w_uv, G.BF16)
@@ -327,8 +332,9 @@ def test_config3_sampled():
         ro, rl = O.latent_attention(qb, lat, 512, case.kq_scale, 4096, [h])
         rv, _ = O.latent_attention_expanded_v(qb, lat, 512, wuv, case.kq_scale, 4096, [h])
         e1, e2, e3 = rel_err(out_lat[b, h], ro[0]), rel_err(v[b, h], rv[0]), abs(lse[b, h] - rl[0])
-        say(f"  (b={b}, h={h}) out_lat {e1:.2e} v {e2:.2e} lse {e3:.2e}")
-        assert e1 <= 2e-2 and e2 <= 2e-2 and e3 <= 2e-2
+        e4, e5 = rel_err(vf[b, h], rv[0]), abs(lsef[b, h] - rl[0])
+        say(f"  (b={b}, h={h}) out_lat {e1:.2e} v {e2:.2e} lse {e3:.2e} fused v {e4:.2e} lse {e5:.2e}")
+        assert e1 <= 2e-2 and e2 <= 2e-2 and e3 <= 2e-2 and e4 <= 2e-2 and e5 <= 2e-2
 
 
 @pytest.mark.slow
