@@ -547,6 +547,7 @@ __device__ __forceinline__ void block_barrier() {
 struct TileSrc {
   const char* p;
   int last;
+  int lastb;  // byte offset of the last visible row from row 0
 };
 
 __device__ __forceinline__ TileSrc tile_src(const Args& a, int b, int t0, int len) {
@@ -559,6 +560,7 @@ __device__ __forceinline__ TileSrc tile_src(const Args& a, int b, int t0, int le
     s.p = (const char*)(a.cache + dense_row(m, b, t0, WD));
   }
   s.last = len - 1 - t0;
+  s.lastb = s.last * (WD * 2);
   return s;
 }
 
@@ -718,9 +720,10 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int len, in
   auto load_tile = [&](const TileSrc& s, int boff, int k) {
     char* buf = smem + boff;
     if (k < 4) {
+      // the row offset (clamped to the last visible row) rides in the lane offset; the base is the tile's
       const int ld = wv + NW * k;
-      const int row = ld < s.last ? ld : s.last;
-      dma16_tile<STREAM>(s.p + (size_t)row * (WD * 2), (uint32_t)(dofs ^ (sC(4 * k) << 4)), lds_addr(buf + ld * 1024));
+      const int rowb = ld * (WD * 2) < s.lastb ? ld * (WD * 2) : s.lastb;
+      dma16_tile<STREAM>(s.p, (uint32_t)((dofs ^ (sC(4 * k) << 4)) + rowb), lds_addr(buf + ld * 1024));
     } else if (wv < 2) {
       const int row = s.last >= TILE - 1 ? rrow : (rrow < s.last ? rrow : s.last);
       dma16_tile<STREAM>(s.p, (uint32_t)(row * (WD * 2) + rdofs), lds_addr(buf + C_BYTES + wv * 1024));
