@@ -721,8 +721,12 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int len, in
     char* buf = smem + boff;
     if (k < 4) {
       // the row offset (clamped to the last visible row) rides in the lane offset; the base is the tile's
+      // (wvb is made opaque here so that the four rows' offsets are not each kept in a register)
       const int ld = wv + NW * k;
-      const int rowb = ld * (WD * 2) < s.lastb ? ld * (WD * 2) : s.lastb;
+      int wvb = wv * (WD * 2);
+      asm volatile("" : "+s"(wvb));
+      const int rb = wvb + k * NW * (WD * 2);
+      const int rowb = rb < s.lastb ? rb : s.lastb;
       dma16_tile<STREAM>(s.p, (uint32_t)((dofs ^ (sC(4 * k) << 4)) + rowb), lds_addr(buf + ld * 1024));
     } else if (wv < 2) {
       const int row = s.last >= TILE - 1 ? rrow : (rrow < s.last ? rrow : s.last);
