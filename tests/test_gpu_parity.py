@@ -146,6 +146,24 @@ def test_decode_up_v(dtype, H, d_v, lens, paged, workers):
     assert rel_err(got, two) <= TOL[dtype]
 
 
+def test_decode_up_v_events_and_no_lse():
+    """The combined call with timing events and without an lse output gives
+    the same v as the plain call, bit for bit (the same kernels run; only the
+    lse stores are skipped), and the events take a positive interval."""
+    case = G.decode_case(3, 128, 512, 64, [700, 0, 1000], G.BF16, seed=9, d_v=128)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    q, cache, w = to_dev(case.q, G.BF16), to_dev(case.cache, G.BF16), to_dev(case.w_uv, G.BF16)
+    lens = torch.from_numpy(case.lens.astype(np.int32)).cuda()
+    v0, lse0 = M.latent_decode_up_v(q, cache, lens, 512, case.kq_scale, w, num_workers=6)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    v1, lse1 = M.latent_decode_up_v(q, cache, lens, 512, case.kq_scale, w, num_workers=6, want_lse=False,
+                                    timing_events=ev)
+    torch.cuda.synchronize()
+    assert lse1 is None and torch.equal(v0, v1)
+    assert ev[0].elapsed_time(ev[1]) > 0
+    assert torch.all(v0[1] == 0) and torch.all(torch.isneginf(lse0[1]))  # the empty row
+
+
 @pytest.mark.parametrize("workers", [4, 1])
 def test_decode_up_v_large_logits(workers):
     """The recompute path of overflowing rows under the fused merge."""
