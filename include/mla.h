@@ -148,9 +148,12 @@ int mla_latent_decode(const void* q, const void* latent_cache,
  *   w_uv [n_heads, d_v, d_c] as in mla_up_v; lse as in mla_latent_decode.
  * All other arguments as mla_latent_decode. workspace: at least
  *   mla_latent_decode_up_v_workspace(batch, n_heads, d_c, num_workers)
- *   bytes (the decode workspace plus room for out_lat). With bf16, d_c = 512
- *   and d_v = 128 the merge of split rows and the up-projection run as one
- *   kernel; otherwise the call runs decode, combine and up-projection.
+ *   bytes (the decode workspace plus room for out_lat). When the attention
+ *   runs on its bf16 MFMA kernel (d_c = 512, d_r = 64, n_heads a multiple of
+ *   32 up to 128, page_size a multiple of 16, 16-byte aligned q, cache, w_uv
+ *   and out) and d_v = 128, the merge of split rows and the up-projection
+ *   run as one kernel; otherwise the call runs decode, combine and
+ *   up-projection. Results agree either way up to rounding order.
  * Limits: as mla_latent_decode and mla_up_v (d_v <= 4096).
  * ------------------------------------------------------------------------- */
 size_t mla_latent_decode_up_v_workspace(int batch, int n_heads, int d_c, int num_workers);
