@@ -19,46 +19,20 @@ namespace mla {
 //
 // Eight waves in two roles, so that neither role's loads queue behind the
 // other's (a wave's loads complete in issue order): waves 0-3 build A (row
-// information with eight lanes per row, then the rows' partial outputs, four
-// rows and up to eight parts each per batch of loads); waves 4-7 stream W_UV[h] through
-// a ring of four 64-wide K slices in LDS and own the MFMA, one 32-column
+// information with eight lanes per row, then the rows' partial outputs, two
+// rows and up to eight parts each per batch of loads); waves 4-7 load their
+// W_UV[h] operands straight into registers and own the MFMA, one 32-column
 // block of v each.
 namespace fu {
 constexpr int FR = 32;                        // rows per workgroup
 constexpr int FK = 512;                       // d_c
 constexpr int FV = 128;                       // d_v (one 32-column block per MFMA wave)
-constexpr int FSL = 64;                       // K slice
-constexpr int FNB = 4;                        // W slice buffers
-constexpr int NSL = FK / FSL;                 // 8 slices
 constexpr int FPW = 8;                        // part weights kept per row (more parts: weights from HBM)
 constexpr int A_ROW = FK * 2;                 // 1 KiB per A row
-constexpr int W_SLICE = FV * FSL * 2;         // 16 KiB
-constexpr int LDS_W = FR * A_ROW;             // A tile first (32 KiB), then the W ring
-constexpr int FSMEM = LDS_W + FNB * W_SLICE;  // 96 KiB
+constexpr int FSMEM = FR * A_ROW;             // the A tile (32 KiB), then the output staging
 
 // A row r, 16-byte chunk c at chunk c ^ (r & 7) (MFMA operand reads of 32 rows spread over the banks)
 __device__ __forceinline__ int a_off(int r, int c) { return r * A_ROW + ((c ^ (r & 7)) << 4); }
-// W slice: column j (128 B of K) chunk c at chunk c ^ (j & 7)
-__device__ __forceinline__ int w_off(int j, int c) { return j * (FSL * 2) + ((c ^ (j & 7)) << 4); }
-
-// a pointer the compiler keeps in vector registers, made an SGPR operand (its value is the same in every lane)
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  const uint64_t u = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ void fdma16(const void* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(gbase), "s"(lds) : "memory");
-}
-// wait until at most n (a multiple of 4, 0..12) of this wave's loads are in flight
-__device__ __forceinline__ void wait_w(int n) {
-  if (n >= 12) __builtin_amdgcn_s_waitcnt(12 | (7 << 4) | (15 << 8));
-  else if (n >= 8) __builtin_amdgcn_s_waitcnt(8 | (7 << 4) | (15 << 8));
-  else if (n >= 4) __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8));
-  else __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-}
-
 __global__ __launch_bounds__(512, 1) void upv_merge_kernel(Plan pl, int H, const bf16* lat, const bf16* w_uv,
                                                            bf16* v, float* lse) {
   __shared__ __attribute__((aligned(1024))) char smem[FSMEM];
@@ -72,22 +46,14 @@ __global__ __launch_bounds__(512, 1) void upv_merge_kernel(Plan pl, int H, const
   const bool mw = wv >= 4;  // MFMA / W wave
   const int mwv = wv - 4;
 
-  // W_UV[h] slice sl: column j = 0..127, K 64 sl .. 64 sl + 63: 16 loads of 1 KiB, 4 per MFMA wave
-  auto issue_w = [&](int sl) {
-    char* buf = smem + LDS_W + (sl % FNB) * W_SLICE;
-    const void* gb = uniform_ptr(w_uv + (size_t)h * FV * FK + sl * FSL);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ld = mwv * 4 + i;
-      const int p = ld * 64 + lane;
-      const int j = p >> 3, c = p & 7;
-      const int cs = c ^ (j & 7);  // this lane's LDS slot holds global chunk cs
-      fdma16(gb, (uint32_t)((j * FK + cs * 8) * 2), (uint32_t)(uintptr_t)(const MLA_LDS char*)(buf + ld * 1024));
-    }
-  };
+  // MFMA waves: the W_UV[h] operands of their 32 columns over the whole K extent go straight
+  // to registers (32 loads of 16 bytes per lane, all issued before anything waits), in the
+  // 32x32x16 B layout: lane l holds column 32 mwv + l % 32, K 16 ks + 8 (l / 32) .. + 7
+  bf16x8 bw[FK / 16];
   if (mw) {
+    const bf16* wc = w_uv + ((size_t)h * FV + mwv * 32 + (lane & 31)) * FK + 8 * (lane >> 5);
 #pragma unroll
-    for (int sl = 0; sl < FNB; ++sl) issue_w(sl);
+    for (int ks = 0; ks < FK / 16; ++ks) bw[ks] = *(const bf16x8*)(wc + 16 * ks);
   } else {
     // row information: eight lanes per row, lane k reads the lse of parts k, k + 8, ...
     const int row = tid >> 3, k = tid & 7, r = n0 + row;
@@ -146,12 +112,12 @@ __global__ __launch_bounds__(512, 1) void upv_merge_kernel(Plan pl, int H, const
   __syncthreads();
 
   if (!mw) {
-    // A tile: wave wv builds rows 8 wv .. 8 wv + 7, lane = 16-byte chunk. Per batch of four
+    // A tile: wave wv builds rows 8 wv .. 8 wv + 7, lane = 16-byte chunk. Per batch of two
     // rows: their plan entries into scalar registers first, then the loads of up to eight
     // sources per row back to back (into zeroed registers, so that no skipped load leaves a
     // register the compiler could reuse while another load is in flight), then the sums.
     const bf16* po = (const bf16*)pl.part_o;
-    constexpr int RB = 4;
+    constexpr int RB = 2;
 #pragma unroll
     for (int rr = 0; rr < 8; rr += RB) {
       int kind[RB], s0[RB], w0[RB], n[RB];
@@ -211,28 +177,15 @@ __global__ __launch_bounds__(512, 1) void upv_merge_kernel(Plan pl, int H, const
     }
   }
 
-  // v^T block: MFMA wave mwv owns columns 32 mwv .. 32 mwv + 31 of all 32 rows. Slice sl is
-  // waited for, then one barrier: slice sl and the A tile are in LDS, and every wave is done
-  // with slice sl - 1, whose buffer then takes slice sl + 3.
+  // v^T block: MFMA wave mwv owns columns 32 mwv .. 32 mwv + 31 of all 32 rows
   f32x16 acc = f32x16{};
   const int g = lane >> 5;
-  for (int sl = 0; sl < NSL; ++sl) {
-    if (mw) {
-      const int last = sl == 0 ? FNB - 1 : (sl + FNB - 2 < NSL - 1 ? sl + FNB - 2 : NSL - 1);  // last slice issued
-      wait_w(4 * (last - sl));
-    }
-    __syncthreads();
-    if (mw) {
-      if (sl >= 1 && sl + FNB - 1 < NSL) issue_w(sl + FNB - 1);
-      const char* wb = smem + LDS_W + (sl % FNB) * W_SLICE;
+  __syncthreads();  // the A tile is complete
+  if (mw) {
 #pragma unroll
-      for (int ks = 0; ks < FSL / 16; ++ks) {
-        const int row = lane & 31, kc = sl * (FSL / 8) + 2 * ks + g;  // A: row, K chunk (of 64)
-        const bf16x8 af = *(const MLA_LDS bf16x8*)(smem + a_off(row, kc));
-        const int j = mwv * 32 + (lane & 31), wc = 2 * ks + g;      // W: column, K chunk of the slice
-        const bf16x8 bw = *(const MLA_LDS bf16x8*)(wb + w_off(j, wc));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bw, acc, 0, 0, 0);
-      }
+    for (int ks = 0; ks < FK / 16; ++ks) {
+      const bf16x8 af = *(const MLA_LDS bf16x8*)(smem + a_off(lane & 31, 2 * ks + g));  // row, K chunk
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bw[ks], acc, 0, 0, 0);
     }
   }
   __syncthreads();  // every MFMA wave is done with the A tile
