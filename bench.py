@@ -121,8 +121,8 @@ def cpu_baseline(case, budget_s):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(decode would shard by sequence, see DESIGN.md); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(decode would shard by sequence); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -20,7 +20,7 @@ Sources (the pages are cited by title and part, never by line):
              (per-head k, v from c) and inference form (absorbed q, shared
              key [c, k_pe], value c, causal sum over i <= t).
 
-Readings adopted where the pages are silent (each listed in the design doc):
+Readings adopted where the pages are silent:
   * logits are scaled by kq_scale = 1/sqrt(d_nope + d_r) ([ferrox] module
     doc); the tutorial's formula omits the scale and the notebook has no
     softmax at all;
