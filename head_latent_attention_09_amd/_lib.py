@@ -8,7 +8,6 @@ been built; there is no fallback implementation.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -86,6 +85,43 @@ def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+def _tensor(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _like(ref, t, name, shape=None, dtype=None):
+    """t must sit on ref's device, have `dtype` (default: ref's) and, when
+    given, exactly `shape` (None entries match any size)."""
+    _tensor(t, name)
+    if t.device != ref.device:
+        raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+    want = ref.dtype if dtype is None else dtype
+    if t.dtype != want:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {want}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(g) != int(w) for g, w in zip(t.shape, shape)):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _ndim(t, name, n):
+    _tensor(t, name)
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+    return t
+
+
+def _on_gpu(*named):
+    """Last check before a launch: every tensor is device memory."""
+    for t, name in named:
+        if t is not None:
+            _dev(t, name)
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
@@ -116,27 +152,39 @@ def absorb_q(q_nope, q_pe, w_uk, out=None):
     """q[n,h,:d_c] = W_UK[h]^T q_nope[n,h,:]; q[n,h,d_c:] = q_pe[n,h,:].
 
     q_nope [N,H,d_nope], q_pe [N,H,d_r] (or None), w_uk [H,d_nope,d_c]."""
-    _dev(q_nope, "q_nope"), _dev(w_uk, "w_uk")
+    _ndim(q_nope, "q_nope", 3)
     N, H, d_nope = q_nope.shape
+    _dtype_code(q_nope)
+    _ndim(w_uk, "w_uk", 3)
     d_c = w_uk.shape[2]
-    d_r = 0 if q_pe is None else q_pe.shape[2]
+    _like(q_nope, w_uk, "w_uk", (H, d_nope, d_c))
+    d_r = 0
     if q_pe is not None:
-        _dev(q_pe, "q_pe")
+        _ndim(q_pe, "q_pe", 3)
+        d_r = q_pe.shape[2]
+        _like(q_nope, q_pe, "q_pe", (N, H, d_r))
     if out is None:
         out = torch.empty((N, H, d_c + d_r), dtype=q_nope.dtype, device=q_nope.device)
-    _check("mla_absorb_q", lib.mla_absorb_q(_ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(_dev(out, "out")),
+    _like(q_nope, out, "out", (N, H, d_c + d_r))
+    _on_gpu((q_nope, "q_nope"), (q_pe, "q_pe"), (w_uk, "w_uk"), (out, "out"))
+    _check("mla_absorb_q", lib.mla_absorb_q(_ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(out),
                                             N, H, d_nope, d_c, d_r, _dtype_code(q_nope), _stream()))
     return out
 
 
 def up_v(out_lat, w_uv, out=None):
     """out[n,h,i] = sum_j W_UV[h,i,j] out_lat[n,h,j]; out_lat [N,H,d_c], w_uv [H,d_v,d_c]."""
-    _dev(out_lat, "out_lat"), _dev(w_uv, "w_uv")
+    _ndim(out_lat, "out_lat", 3)
     N, H, d_c = out_lat.shape
+    _dtype_code(out_lat)
+    _ndim(w_uv, "w_uv", 3)
     d_v = w_uv.shape[1]
+    _like(out_lat, w_uv, "w_uv", (H, d_v, d_c))
     if out is None:
         out = torch.empty((N, H, d_v), dtype=out_lat.dtype, device=out_lat.device)
-    _check("mla_up_v", lib.mla_up_v(_ptr(out_lat), _ptr(w_uv), _ptr(_dev(out, "out")), N, H, d_c, d_v,
+    _like(out_lat, out, "out", (N, H, d_v))
+    _on_gpu((out_lat, "out_lat"), (w_uv, "w_uv"), (out, "out"))
+    _check("mla_up_v", lib.mla_up_v(_ptr(out_lat), _ptr(w_uv), _ptr(out), N, H, d_c, d_v,
                                     _dtype_code(out_lat), _stream()))
     return out
 
@@ -149,10 +197,49 @@ def prefill_workspace_bytes(batch, s_q, n_heads, d_c, num_workers=0) -> int:
     return int(lib.mla_latent_prefill_causal_workspace(batch, s_q, n_heads, d_c, num_workers))
 
 
-def _workspace(nbytes, device, workspace):
-    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
-        return workspace
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+def _workspace(nbytes, ref, workspace):
+    if workspace is not None:
+        _tensor(workspace, "workspace")
+        if workspace.device != ref.device:
+            raise ValueError(f"workspace is on {workspace.device}, expected {ref.device}")
+        if workspace.numel() * workspace.element_size() >= nbytes:
+            return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=ref.device)
+
+
+def _ws_bytes(ws):
+    return ws.numel() * ws.element_size()
+
+
+def _decode_inputs(q, cache, seq_lens, d_c, block_table, num_pages, lse, want_lse):
+    """Checks shared by the decode wrappers; returns the cache geometry and lse."""
+    _ndim(q, "q", 3)
+    B, H, W = q.shape
+    _dtype_code(q)
+    if not 0 < d_c <= W:
+        raise ValueError(f"d_c = {d_c} must be in 1..{W} (the query row width)")
+    _ndim(cache, "cache", 3)
+    _like(q, cache, "cache", (None, None, W))
+    _like(q, seq_lens, "seq_lens", (B,), dtype=torch.int32)
+    if block_table is not None:
+        _ndim(block_table, "block_table", 2)
+        _like(q, block_table, "block_table", (B, None), dtype=torch.int32)
+        page_size, max_pages = cache.shape[1], block_table.shape[1]
+        if num_pages is None:
+            num_pages = cache.shape[0]
+        if not 0 < num_pages <= cache.shape[0]:
+            raise ValueError(f"num_pages = {num_pages} must be in 1..{cache.shape[0]} (the pool's pages)")
+        stride = 0
+    else:
+        if cache.shape[0] < B:
+            raise ValueError(f"dense cache holds {cache.shape[0]} sequences, batch is {B}")
+        page_size = max_pages = num_pages = 0
+        stride = cache.shape[1]
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _like(q, lse, "lse", (B, H), dtype=torch.float32)
+    return B, H, W, stride, page_size, max_pages, num_pages, lse
 
 
 def latent_decode(q, cache, seq_lens, d_c, kq_scale, block_table=None, num_pages=None, num_workers=0,
@@ -161,32 +248,21 @@ def latent_decode(q, cache, seq_lens, d_c, kq_scale, block_table=None, num_pages
 
     q [B,H,W] rows [q_abs | q_pe]; seq_lens int32 [B]; block_table int32
     [B,max_pages] or None. Returns (out_lat [B,H,d_c], lse [B,H] or None)."""
-    _dev(q, "q"), _dev(cache, "cache"), _dev(seq_lens, "seq_lens")
-    B, H, W = q.shape
+    B, H, W, stride, page_size, max_pages, num_pages, lse = _decode_inputs(
+        q, cache, seq_lens, d_c, block_table, num_pages, lse, want_lse)
     d_r = W - d_c
-    if seq_lens.dtype != torch.int32:
-        raise TypeError("seq_lens must be int32")
-    if block_table is not None:
-        _dev(block_table, "block_table")
-        if block_table.dtype != torch.int32:
-            raise TypeError("block_table must be int32")
-        page_size, max_pages = cache.shape[1], block_table.shape[1]
-        num_pages = cache.shape[0] if num_pages is None else num_pages
-        stride = 0
-    else:
-        page_size = max_pages = num_pages = 0
-        stride = cache.shape[1]
     if out is None:
         out = torch.empty((B, H, d_c), dtype=q.dtype, device=q.device)
-    if lse is None and want_lse:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _like(q, out, "out", (B, H, d_c))
+    _on_gpu((q, "q"), (cache, "cache"), (seq_lens, "seq_lens"), (block_table, "block_table"), (out, "out"),
+            (lse, "lse"))
     nb = decode_workspace_bytes(B, H, d_c, num_workers)
-    ws = _workspace(nb, q.device, workspace)
+    ws = _workspace(nb, q, workspace)
     ev = _events(timing_events)
     _check("mla_latent_decode", lib.mla_latent_decode(
         _ptr(q), _ptr(cache), _ptr(seq_lens), _ptr(block_table), B, H, d_c, d_r, stride, page_size,
-        max_pages, num_pages, float(kq_scale), _dtype_code(q), _ptr(_dev(out, "out")), _ptr(lse),
-        _ptr(ws), ws.numel(), num_workers, None if ev is None else ev[0], _stream()))
+        max_pages, num_pages, float(kq_scale), _dtype_code(q), _ptr(out), _ptr(lse),
+        _ptr(ws), _ws_bytes(ws), num_workers, None if ev is None else ev[0], _stream()))
     return out, lse
 
 
@@ -199,33 +275,24 @@ def latent_decode_up_v(q, cache, seq_lens, d_c, kq_scale, w_uv, block_table=None
     """Absorbed decode and the W_UV up-projection in one call.
 
     As latent_decode, plus w_uv [H,d_v,d_c]. Returns (v [B,H,d_v], lse [B,H] or None)."""
-    _dev(q, "q"), _dev(cache, "cache"), _dev(seq_lens, "seq_lens"), _dev(w_uv, "w_uv")
-    B, H, W = q.shape
+    B, H, W, stride, page_size, max_pages, num_pages, lse = _decode_inputs(
+        q, cache, seq_lens, d_c, block_table, num_pages, lse, want_lse)
     d_r = W - d_c
+    _ndim(w_uv, "w_uv", 3)
     d_v = w_uv.shape[1]
-    if seq_lens.dtype != torch.int32:
-        raise TypeError("seq_lens must be int32")
-    if block_table is not None:
-        _dev(block_table, "block_table")
-        if block_table.dtype != torch.int32:
-            raise TypeError("block_table must be int32")
-        page_size, max_pages = cache.shape[1], block_table.shape[1]
-        num_pages = cache.shape[0] if num_pages is None else num_pages
-        stride = 0
-    else:
-        page_size = max_pages = num_pages = 0
-        stride = cache.shape[1]
+    _like(q, w_uv, "w_uv", (H, d_v, d_c))
     if out is None:
         out = torch.empty((B, H, d_v), dtype=q.dtype, device=q.device)
-    if lse is None and want_lse:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _like(q, out, "out", (B, H, d_v))
+    _on_gpu((q, "q"), (cache, "cache"), (seq_lens, "seq_lens"), (block_table, "block_table"), (w_uv, "w_uv"),
+            (out, "out"), (lse, "lse"))
     nb = decode_up_v_workspace_bytes(B, H, d_c, num_workers)
-    ws = _workspace(nb, q.device, workspace)
+    ws = _workspace(nb, q, workspace)
     ev = _events(timing_events)
     _check("mla_latent_decode_up_v", lib.mla_latent_decode_up_v(
         _ptr(q), _ptr(cache), _ptr(seq_lens), _ptr(block_table), B, H, d_c, d_r, stride, page_size,
-        max_pages, num_pages, float(kq_scale), _ptr(w_uv), d_v, _dtype_code(q), _ptr(_dev(out, "out")), _ptr(lse),
-        _ptr(ws), ws.numel(), num_workers, None if ev is None else ev[0], _stream()))
+        max_pages, num_pages, float(kq_scale), _ptr(w_uv), d_v, _dtype_code(q), _ptr(out), _ptr(lse),
+        _ptr(ws), _ws_bytes(ws), num_workers, None if ev is None else ev[0], _stream()))
     return out, lse
 
 
@@ -233,36 +300,46 @@ def latent_prefill_causal(q, cache, d_c, kq_scale, num_workers=0, out=None, lse=
                           workspace=None, timing_events=None):
     """Causal prefill: q [B,S_q,H,W], cache [B,S_kv,W]; query i sees t <= i + S_kv - S_q.
     Returns (out_lat [B,S_q,H,d_c], lse [B,S_q,H] or None)."""
-    _dev(q, "q"), _dev(cache, "cache")
+    _ndim(q, "q", 4)
     B, S_q, H, W = q.shape
+    _dtype_code(q)
+    if not 0 < d_c <= W:
+        raise ValueError(f"d_c = {d_c} must be in 1..{W} (the query row width)")
+    _ndim(cache, "cache", 3)
+    _like(q, cache, "cache", (B, None, W))
     S_kv = cache.shape[1]
     d_r = W - d_c
     if out is None:
         out = torch.empty((B, S_q, H, d_c), dtype=q.dtype, device=q.device)
+    _like(q, out, "out", (B, S_q, H, d_c))
     if lse is None and want_lse:
         lse = torch.empty((B, S_q, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _like(q, lse, "lse", (B, S_q, H), dtype=torch.float32)
+    _on_gpu((q, "q"), (cache, "cache"), (out, "out"), (lse, "lse"))
     nb = prefill_workspace_bytes(B, S_q, H, d_c, num_workers)
-    ws = _workspace(nb, q.device, workspace)
+    ws = _workspace(nb, q, workspace)
     ev = _events(timing_events)
     _check("mla_latent_prefill_causal", lib.mla_latent_prefill_causal(
         _ptr(q), _ptr(cache), B, S_q, S_kv, H, d_c, d_r, float(kq_scale), _dtype_code(q),
-        _ptr(_dev(out, "out")), _ptr(lse), _ptr(ws), ws.numel(), num_workers,
+        _ptr(out), _ptr(lse), _ptr(ws), _ws_bytes(ws), num_workers,
         None if ev is None else ev[0], _stream()))
     return out, lse
 
 
 def lse_combine(o_parts, lse_parts, dtype=torch.float32, out=None, want_lse=True):
     """Merge partial softmax results: o_parts [P,R,H,d_c] fp32, lse_parts [P,R,H] fp32."""
-    _dev(o_parts, "o_parts"), _dev(lse_parts, "lse_parts")
+    _ndim(o_parts, "o_parts", 4)
+    if o_parts.dtype != torch.float32:
+        raise TypeError(f"o_parts has dtype {o_parts.dtype}, expected torch.float32")
     P, R, H, d_c = o_parts.shape
+    _like(o_parts, lse_parts, "lse_parts", (P, R, H))
     if out is None:
         out = torch.empty((R, H, d_c), dtype=dtype, device=o_parts.device)
+    _like(o_parts, out, "out", (R, H, d_c), dtype=out.dtype)
+    _dtype_code(out)
     lse = torch.empty((R, H), dtype=torch.float32, device=o_parts.device) if want_lse else None
+    _on_gpu((o_parts, "o_parts"), (lse_parts, "lse_parts"), (out, "out"))
     _check("mla_lse_combine", lib.mla_lse_combine(_ptr(o_parts), _ptr(lse_parts), P, R, H, d_c,
                                                   _dtype_code(out), _ptr(out), _ptr(lse), _stream()))
     return out, lse
-
-
-def kq_scale_for(d_nope: int, d_r: int) -> float:
-    """1/sqrt(d_nope + d_r): the width of the unabsorbed head."""
-    return 1.0 / math.sqrt(d_nope + d_r)

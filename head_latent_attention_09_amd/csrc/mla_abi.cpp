@@ -17,10 +17,22 @@ int elem_size(int dtype) { return dtype == MLA_BF16 ? 2 : 4; }
 bool valid_dtype(int dtype) { return dtype == MLA_F32 || dtype == MLA_BF16; }
 bool aligned(const void* p, int a) { return ((uintptr_t)p % (uintptr_t)a) == 0; }
 
+// Largest worker count: the combine kernels put the split rows (at most one
+// per worker) on the grid's y axis, whose limit is 65535.
+constexpr int kMaxWorkers = 65535;
+
 int resolve_workers(int num_workers) {
   if (num_workers < 0) return MLA_ERR_SHAPE;
+  if (num_workers > kMaxWorkers) return MLA_ERR_UNSUPPORTED;
   if (num_workers > 0) return num_workers;
   return mla_default_workers();
+}
+
+// The plan counts work in int32 units: one per 16-position tile plus a fixed
+// cost of SEG_COST units per non-empty row; the unit total (and prefix sums)
+// must stay far from overflow.
+bool units_fit(int64_t rows, int64_t max_len) {
+  return rows * ((max_len + 15) / 16 + SEG_COST) <= INT32_MAX / 2;
 }
 
 }  // namespace
@@ -136,7 +148,6 @@ static int decode_call(const void* q, const void* latent_cache, const int32_t* s
   if (st != MLA_OK) return st;
   if (!seq_lens) return MLA_ERR_NULL;
   if (!aligned(seq_lens, 4) || (block_table && !aligned(block_table, 4))) return MLA_ERR_ALIGN;
-  const int tile_min = 16;
   int64_t cap;
   if (block_table) {
     if (page_size <= 0 || max_pages <= 0 || num_pages <= 0) return MLA_ERR_SHAPE;
@@ -145,7 +156,7 @@ static int decode_call(const void* q, const void* latent_cache, const int32_t* s
     if (cache_stride < 0) return MLA_ERR_SHAPE;
     cap = cache_stride;
   }
-  if ((int64_t)batch * ((cap + tile_min - 1) / tile_min) > INT32_MAX / 2) return MLA_ERR_UNSUPPORTED;
+  if (!units_fit(batch, cap)) return MLA_ERR_UNSUPPORTED;
   const int G = resolve_workers(num_workers);
   if (G <= 0) return G == 0 ? MLA_ERR_SHAPE : G;
   if (!workspace) return MLA_ERR_WORKSPACE;
@@ -230,7 +241,7 @@ int mla_latent_prefill_causal(const void* q, const void* latent_cache, int batch
   if (rows == 0) return MLA_OK;  // nothing to do; empty tensors may have NULL data
   st = common_attn_checks(q, latent_cache, out_lat, lse, workspace, dtype, kq_scale);
   if (st != MLA_OK) return st;
-  if (rows * ((s_kv + 15) / 16) > INT32_MAX / 2) return MLA_ERR_UNSUPPORTED;
+  if (!units_fit(rows, s_kv)) return MLA_ERR_UNSUPPORTED;
   const int G = resolve_workers(num_workers);
   if (G <= 0) return G == 0 ? MLA_ERR_SHAPE : G;
   if (!workspace) return MLA_ERR_WORKSPACE;

@@ -21,8 +21,8 @@
  *     and contiguous in the innermost dimension. The library never
  *     allocates, frees or synchronises the host in these calls; scratch for
  *     split-sequence partial results comes from the caller's workspace.
- *   - Inputs are never written (the gated-MLA problem statement's "do not
- *     mutate any input tensor"); every element of every output is written.
+ *   - Inputs are never written (the gated-MLA problem statement requires
+ *     the inputs to stay unchanged); every element of every output is written.
  *   - All tensors of one call share `dtype` (MLA_F32 or MLA_BF16);
  *     accumulation is fp32; outputs are in `dtype`; lse outputs are fp32.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
@@ -119,14 +119,16 @@ int mla_up_v(const void* out_lat, const void* w_uv, void* out,
  * workspace / workspace_bytes: device scratch of at least
  *   mla_latent_decode_workspace(batch, n_heads, d_c, num_workers) bytes;
  *   contents on entry are ignored. Concurrent calls need separate workspaces.
- * num_workers: attention workgroups to launch (0 = mla_default_workers()).
- *   Results do not depend on it beyond floating-point rounding.
+ * num_workers: attention workgroups to launch (0 = mla_default_workers(),
+ *   at most 65535). Results do not depend on it beyond floating-point rounding.
  * timing_events: NULL, or a pointer to two hipEvent_t passed with the
  *   attention kernel's launch on `stream`: they take the start and end times
  *   of its dispatch (for profiling; the planning and combine kernels fall
  *   outside them).
  * Limits: d_c <= 1024, d_c + d_r <= 1152, n_heads <= 65535,
- *   page_size >= 1 when paged.
+ *   page_size >= 1 when paged, batch * (ceil(cap / 16) + 12) <= 2^30 - 1
+ *   with cap = cache_stride (dense) or max_pages * page_size (paged): the
+ *   split plan counts 16-position tiles plus a fixed cost per row in int32.
  * ------------------------------------------------------------------------- */
 size_t mla_latent_decode_workspace(int batch, int n_heads, int d_c, int num_workers);
 
@@ -179,7 +181,8 @@ int mla_latent_decode_up_v(const void* q, const void* latent_cache,
  * Queries that see no position (s_q > s_kv) get zeros and lse = -inf.
  * workspace: at least mla_latent_prefill_causal_workspace(batch, s_q,
  *   n_heads, d_c, num_workers) bytes. num_workers, timing_events: as decode.
- * Limits: as decode; batch * s_q <= 2^31 - 1.
+ * Limits: as decode, with batch * s_q rows of cap = s_kv positions;
+ *   batch * s_q <= 2^31 - 1.
  * ------------------------------------------------------------------------- */
 size_t mla_latent_prefill_causal_workspace(int batch, int s_q, int n_heads, int d_c, int num_workers);
 

@@ -6,7 +6,8 @@ baseline leg do. It shares no code with the HIP library: its one dependency
 on this repository is the seeded input generator in `workloads`.
 
 Everything here is plain float64 numpy written from the pages' definitions.
-Each function's pins (tests that tie it to something other than itself) are
-listed in its docstring. No function is "parity unpinned".
+Each function's pins (tests in tests/test_oracle_pins.py that tie it to
+something other than itself: printed values, closed forms, brute force,
+invariances) are listed in its docstring.
 """
 from .mla_oracle import *  # noqa: F401,F403

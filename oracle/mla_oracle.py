@@ -40,7 +40,7 @@ __all__ = [
     "latent_attention_expanded_v", "absorb_query", "up_project",
     "causal_visible", "latent_prefill_causal", "lse_merge",
     "mha_cache_values_per_token", "mla_cache_values_per_token", "cache_ratio",
-    "notebook_split_heads", "notebook_linear_absorbed", "notebook_linear_unabsorbed",
+    "notebook_head_blocks", "notebook_linear_absorbed", "notebook_linear_unabsorbed",
     "notebook_softmax_unabsorbed", "gated_mla",
 ]
 
@@ -271,66 +271,89 @@ def cache_ratio(H, d_head, d_c, d_r):
 # --------------------------------------------------------------------------
 # the RoPE-less notebook ([notebook])
 # --------------------------------------------------------------------------
-def notebook_split_heads(W_uQ, W_uK, W_uV, W_O, h):
-    """Head split of the notebook: [d_c, h*d_h] -> [h, d_c, d_h] by column
-    blocks; W_O [h*d_h, d_model] -> [h, d_h, d_model] by row blocks."""
-    d_c, d_up = np.shape(W_uQ)
-    d_h = d_up // h
+def notebook_head_blocks(W_up, W_out, h):
+    """Per-head blocks of the notebook's weights.
 
-    def cols(W):
-        return _f64(W).reshape(d_c, h, d_h).transpose(1, 0, 2)
-
-    return cols(W_uQ), cols(W_uK), cols(W_uV), _f64(W_O).reshape(h, d_h, -1)
+    The up-projections W_up [d_c, h d_h] hold head s in columns
+    s d_h .. (s+1) d_h - 1 (the head index is the slower of the two factors
+    the column index splits into); the output projection W_out [h d_h, d_model]
+    holds head s in rows s d_h .. (s+1) d_h - 1. Returns (list of [d_c, d_h]
+    blocks, list of [d_h, d_model] blocks).
+    Pinned by: entries tagged with their own column / row index land in the
+    block of their head (tests), and the per-head softmax workload.
+    """
+    W_up, W_out = _f64(W_up), _f64(W_out)
+    d_h = W_up.shape[1] // h
+    ups = [W_up[:, s * d_h:(s + 1) * d_h] for s in range(h)]
+    outs = [W_out[s * d_h:(s + 1) * d_h, :] for s in range(h)]
+    return ups, outs
 
 
 def notebook_linear_absorbed(X, W_dQ, W_dKV, W_uQ, W_uK, W_uV, W_O, C_KV, h):
-    """The notebook's fully absorbed, softmax-free pipeline.
+    """The notebook's fully absorbed, softmax-free computation, from its math.
 
-    W_aQK[h] = W_uQ[h] W_uK[h]^T, W_aVO[h] = W_uV[h] W_O[h]; the new latent
-    X W_dKV is appended to the cache; per head attn = (X W_dQ W_aQK) C^T,
-    out = attn (C W_aVO); final = sum over heads. Returns every array whose
-    shape the notebook prints.
+    For head s: A_QK(s) = U_Q(s) U_K(s)^T ([d_c, d_c]) and
+    A_VO(s) = U_V(s) O(s) ([d_c, d_model]); the cache gains the new latent
+    row x W_dKV; the latent query of head s is (x W_dQ) A_QK(s); its
+    unnormalised "attention" row is that query times every cache row; the
+    head output is that row times (cache A_VO(s)); the result sums the heads.
+    Returns the arrays whose shapes the notebook prints, keyed by its printed
+    labels.
     """
-    uQ, uK, uV, O = notebook_split_heads(W_uQ, W_uK, W_uV, W_O, h)
-    W_aQK = uQ @ uK.transpose(0, 2, 1)
-    W_aVO = uV @ O
-    C = np.vstack([_f64(C_KV), _f64(X) @ _f64(W_dKV)])
-    C_Q = _f64(X) @ _f64(W_dQ) @ W_aQK
-    attn = C_Q @ C.T
-    score = C @ W_aVO
-    out_heads = attn @ score
-    final = out_heads.sum(axis=0)
-    return dict(X=_f64(X), C_Q=C_Q, C_KV=C, W_aQK=W_aQK, W_aVO=W_aVO, final=final)
+    X, W_dQ, W_dKV = _f64(X), _f64(W_dQ), _f64(W_dKV)
+    uQ, O_blocks = notebook_head_blocks(W_uQ, W_O, h)
+    uK, _ = notebook_head_blocks(W_uK, W_O, h)
+    uV, _ = notebook_head_blocks(W_uV, W_O, h)
+    cache = np.vstack([_f64(C_KV), X @ W_dKV])                  # [T, d_c]
+    c_q = X @ W_dQ                                              # [1, d_c]
+    a_qk = np.stack([uQ[s] @ uK[s].T for s in range(h)])        # [h, d_c, d_c]
+    a_vo = np.stack([uV[s] @ O_blocks[s] for s in range(h)])    # [h, d_c, d_model]
+    latent_query = np.stack([c_q @ a_qk[s] for s in range(h)])  # [h, 1, d_c]
+    total = np.zeros((1, O_blocks[0].shape[1]))
+    for s in range(h):
+        weights = latent_query[s] @ cache.T                     # [1, T], no softmax
+        total += weights @ (cache @ a_vo[s])
+    return {"Input Shape": X, "Latent Query": latent_query, "Latent KV Cache": cache,
+            "Absorbed QK Kernel": a_qk, "Absorbed VO Kernel": a_vo, "Final Output Shape": total}
 
 
 def notebook_linear_unabsorbed(X, W_dQ, W_dKV, W_uQ, W_uK, W_uV, W_O, C_KV, h):
-    """The same softmax-free computation without absorption: expand q, k, v per
-    head first, then out_h = (q_h k_h^T) v_h W_O[h], summed over heads."""
-    uQ, uK, uV, O = notebook_split_heads(W_uQ, W_uK, W_uV, W_O, h)
-    C = np.vstack([_f64(C_KV), _f64(X) @ _f64(W_dKV)])
-    cq = _f64(X) @ _f64(W_dQ)
-    final = 0.0
+    """The same softmax-free computation without absorption: per head s,
+    q = (x W_dQ) U_Q(s), k_t = c_t U_K(s), v_t = c_t U_V(s);
+    out_s = sum_t (q . k_t) v_t O(s); summed over heads."""
+    X = _f64(X)
+    uQ, O_blocks = notebook_head_blocks(W_uQ, W_O, h)
+    uK, _ = notebook_head_blocks(W_uK, W_O, h)
+    uV, _ = notebook_head_blocks(W_uV, W_O, h)
+    cache = np.vstack([_f64(C_KV), X @ _f64(W_dKV)])
+    c_q = (X @ _f64(W_dQ))[0]
+    total = np.zeros(O_blocks[0].shape[1])
     for s in range(h):
-        q_s, k_s, v_s = cq @ uQ[s], C @ uK[s], C @ uV[s]
-        final = final + (q_s @ k_s.T) @ v_s @ O[s]
-    return final
+        q = c_q @ uQ[s]
+        for t in range(cache.shape[0]):
+            k_t, v_t = cache[t] @ uK[s], cache[t] @ uV[s]
+            total += float(q @ k_t) * (v_t @ O_blocks[s])
+    return total[None, :]
 
 
 def notebook_softmax_unabsorbed(X, W_dQ, W_dKV, W_uQ, W_uK, W_uV, W_O, C_KV, h, scale):
     """The notebook's workload with softmax attention, computed unabsorbed.
 
-    Per head: q_h = X W_dQ W_uQ[h], k_t,h = c_t W_uK[h], v_t,h = c_t W_uV[h]
-    over the cache with the new token appended (it attends to itself); the
-    softmax uses `scale`. Returns (v [h, d_h], final [d_model] = sum_h v_h W_O[h]).
+    Per head s: q = x W_dQ U_Q(s), k_t = c_t U_K(s), v_t = c_t U_V(s) over the
+    cache with the new token appended (it attends to itself); the softmax
+    uses `scale`. Returns (v [h, d_h], final [d_model] = sum_s v_s O(s)).
     """
-    uQ, uK, uV, O = notebook_split_heads(W_uQ, W_uK, W_uV, W_O, h)
-    C = np.vstack([_f64(C_KV), _f64(X) @ _f64(W_dKV)])
-    cq = (_f64(X) @ _f64(W_dQ))[0]
-    v = np.zeros((h, uV.shape[2]))
-    final = np.zeros(O.shape[2])
+    X = _f64(X)
+    uQ, O_blocks = notebook_head_blocks(W_uQ, W_O, h)
+    uK, _ = notebook_head_blocks(W_uK, W_O, h)
+    uV, _ = notebook_head_blocks(W_uV, W_O, h)
+    cache = np.vstack([_f64(C_KV), X @ _f64(W_dKV)])
+    c_q = (X @ _f64(W_dQ))[0]
+    v = np.zeros((h, uV[0].shape[1]))
+    final = np.zeros(O_blocks[0].shape[1])
     for s in range(h):
-        v[s], _ = attend_one_head(cq @ uQ[s], C @ uK[s], C @ uV[s], scale, C.shape[0])
-        final += v[s] @ O[s]
+        v[s], _ = attend_one_head(c_q @ uQ[s], cache @ uK[s], cache @ uV[s], scale, cache.shape[0])
+        final += v[s] @ O_blocks[s]
     return v, final
 
 

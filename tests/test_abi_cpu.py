@@ -102,6 +102,19 @@ def test_decode_validation():
     assert _decode(B=0, dtype=5) == -3 and _decode(B=0, scale=math.nan) == -7 and _decode(B=0, H=0) == -2
 
 
+def test_decode_unit_and_worker_limits():
+    """The plan's int32 unit count includes the fixed cost per row: short rows
+    in great number are rejected even when their tiles alone would fit; more
+    than 65535 workers are rejected (the combine grid's y axis) before any launch."""
+    # 16-position rows: one tile + 12 fixed units each; 2^30 / 13 rows overflow
+    # the budget although 2^30 / 1 tiles would not
+    assert _decode(B=90_000_000, stride=16) == -4
+    assert _decode(B=60_000_000, stride=16, ws=None) == -5   # fits: the next check (workspace) fails
+    assert _decode(workers=65536) == -4
+    assert _decode(workers=70000) == -4
+    assert M.decode_workspace_bytes(2, 4, 16, 70000) == 0
+
+
 def _decode_up_v(**kw):
     a = dict(q=FAKE, cache=FAKE, lens=FAKE, table=None, B=2, H=4, d_c=16, d_r=4, stride=8, page=0,
              max_pages=0, num_pages=0, scale=0.3, w=FAKE, d_v=8, dtype=M.MLA_F32, out=FAKE, lse=FAKE, ws=FAKE,
@@ -146,6 +159,9 @@ def test_prefill_validation():
     assert call(B=0) == 0 and call(S_q=0) == 0
     assert call(B=0, q=None, cache=None, out=None, ws=None) == 0
     assert call(B=70000, S_q=70000) == -4
+    # unit budget with the fixed cost per row (query rows of one tile each)
+    assert call(B=1, S_q=90_000_000, S_kv=16) == -4
+    assert call(workers=70000) == -4
 
 
 def test_lse_combine_validation():

@@ -514,9 +514,14 @@ def test_ferrox_shape_chain(dtype):
 def test_config1_notebook_chain():
     d = G.config1_notebook(0)
     scale = 1.0 / math.sqrt(d.d_h)
-    uQ, uK, uV, Ow = O.notebook_split_heads(d.W_uQ, d.W_uK, d.W_uV, d.W_O, d.H)
+    H, dh = d.H, d.d_h
+    # head s owns columns s*d_h .. (s+1)*d_h - 1 of the up-projections and the
+    # same rows of W_O (sliced here, independently of the oracle)
+    blk = lambda W: np.stack([W[:, s * dh:(s + 1) * dh] for s in range(H)])   # [H, d_c, d_h]
+    uK, uV = blk(d.W_uK), blk(d.W_uV)
+    Ow = np.stack([d.W_O[s * dh:(s + 1) * dh] for s in range(H)])            # [H, d_h, d_model]
     cache = np.vstack([d.C_KV, d.X @ d.W_dKV])                 # host-side append of the new latent
-    q_nope = ((d.X @ d.W_dQ)[0] @ uQ)                           # [H, d_h]
+    q_nope = np.einsum("i,hij->hj", (d.X @ d.W_dQ)[0], blk(d.W_uQ))          # [H, d_h]
     st = lambda a: G.storage(a, G.F32)
     q = M.absorb_q(to_dev(st(q_nope[None]), G.F32), None, to_dev(st(uK.transpose(0, 2, 1)), G.F32))
     lens = torch.tensor([cache.shape[0]], dtype=torch.int32).cuda()

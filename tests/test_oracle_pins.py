@@ -171,18 +171,56 @@ def test_notebook_printed_shapes(golden_dir):
 
 def test_notebook_linear_absorption_is_associativity():
     d = G.config1_notebook(0)
-    a = O.notebook_linear_absorbed(d.X, d.W_dQ, d.W_dKV, d.W_uQ, d.W_uK, d.W_uV, d.W_O, d.C_KV, d.H)["final"]
+    a = O.notebook_linear_absorbed(d.X, d.W_dQ, d.W_dKV, d.W_uQ, d.W_uK, d.W_uV, d.W_O, d.C_KV,
+                                   d.H)["Final Output Shape"]
     u = O.notebook_linear_unabsorbed(d.X, d.W_dQ, d.W_dKV, d.W_uQ, d.W_uK, d.W_uV, d.W_O, d.C_KV, d.H)
     assert np.max(np.abs(a - u)) <= 1e-10 * np.max(np.abs(u))
 
 
+def test_notebook_head_blocks_are_head_major():
+    """The notebook splits the up-projection columns head-major (reshape to
+    (d_c, h, d_h), heads to the front): head s owns columns s*d_h .. s*d_h+d_h-1,
+    and the output projection's rows likewise. Entries tagged with their own
+    column (row) index must land in their head's block, in order; a d_h-major
+    split (column j -> head j % h) puts them elsewhere."""
+    d_c, h, d_h, d_model = 4, 3, 5, 7
+    cols = np.tile(np.arange(h * d_h, dtype=np.float64), (d_c, 1))          # W[i, j] = j
+    rows = np.tile(np.arange(h * d_h, dtype=np.float64)[:, None], (1, d_model))  # W_O[i, j] = i
+    ups, outs = O.notebook_head_blocks(cols, rows, h)
+    assert len(ups) == h and len(outs) == h
+    for s in range(h):
+        want = np.arange(s * d_h, (s + 1) * d_h, dtype=np.float64)
+        assert ups[s].shape == (d_c, d_h) and outs[s].shape == (d_h, d_model)
+        assert np.all(ups[s] == want[None, :]) and np.all(outs[s] == want[:, None])
+    # the notebook's own reshape/transpose of a tagged matrix gives the same blocks
+    nb = cols.reshape(d_c, h, d_h).transpose(1, 0, 2)
+    for s in range(h):
+        np.testing.assert_array_equal(ups[s], nb[s])
+
+
+def test_notebook_head_split_decides_the_softmax_workload():
+    """With a d_h-major split the softmax workload changes: the result is
+    sensitive to the split (so the pin above is the one that fixes it)."""
+    d = G.config1_notebook(0)
+    scale = 1.0 / math.sqrt(d.d_h)
+    v, final = O.notebook_softmax_unabsorbed(d.X, d.W_dQ, d.W_dKV, d.W_uQ, d.W_uK, d.W_uV, d.W_O,
+                                             d.C_KV, d.H, scale)
+    perm = np.arange(d.H * d.d_h).reshape(d.d_h, d.H).T.reshape(-1)    # column j -> head j % h
+    v2, final2 = O.notebook_softmax_unabsorbed(d.X, d.W_dQ, d.W_dKV, d.W_uQ[:, perm], d.W_uK[:, perm],
+                                               d.W_uV[:, perm], d.W_O[perm], d.C_KV, d.H, scale)
+    assert np.max(np.abs(final - final2)) > 1e-3 * np.max(np.abs(final))
+
+
 def _config1_path_inputs(d):
-    """Config 1 expressed in the path's layouts (host-side preparation)."""
-    uQ, uK, uV, Ow = O.notebook_split_heads(d.W_uQ, d.W_uK, d.W_uV, d.W_O, d.H)
+    """Config 1 expressed in the path's layouts (host-side preparation; the
+    head blocks are sliced here directly, not through the oracle)."""
+    H, dh = d.H, d.d_h
+    blk = lambda W: np.stack([W[:, s * dh:(s + 1) * dh] for s in range(H)])   # head-major column blocks
     cache = np.vstack([d.C_KV, d.X @ d.W_dKV])            # 6 rows, d_r = 0
-    q_nope = ((d.X @ d.W_dQ)[0] @ uQ)                      # [H, d_h]
-    w_uk = uK.transpose(0, 2, 1)                           # [H, d_h, d_c]
-    w_uv = uV.transpose(0, 2, 1)                           # [H, d_h, d_c]
+    q_nope = np.einsum("i,hij->hj", (d.X @ d.W_dQ)[0], blk(d.W_uQ))      # [H, d_h]
+    w_uk = blk(d.W_uK).transpose(0, 2, 1)                  # [H, d_h, d_c]
+    w_uv = blk(d.W_uV).transpose(0, 2, 1)                  # [H, d_h, d_c]
+    Ow = np.stack([d.W_O[s * dh:(s + 1) * dh] for s in range(H)])          # [H, d_h, d_model]
     return cache, q_nope, w_uk, w_uv, Ow
 
 
@@ -227,6 +265,60 @@ def test_gated_shape_examples(golden_dir):
         assert list(res["output"].shape) == ex["output_shape"]
         assert list(res["latent_cache"].shape) == ex["latent_cache_shape"]
         np.testing.assert_array_equal(x, x0)  # inputs not mutated
+
+
+def _sig(z):
+    return 1.0 / (1.0 + math.exp(-z))
+
+
+def _gated_two_positions(causal):
+    """Two positions, D = 4, one head (D_h = 4, scale 1/2), latent width 1.
+    W_q = I, so Q_i = x_i; W_c picks channel 0, so C_j = x_j[0]; W_k = ones
+    (K_j = C_j (1,1,1,1)); W_v picks the latent into channel 0 (V_j = (C_j, 0,
+    0, 0)); gate weights 0 (sigmoid 1/2); W_o = I.
+    x_0 = (1,0,0,0), x_1 = (2,1,0,1): C = (1, 2); logit(i, j) = sum(x_i) C_j / 2.
+    Row 1 sees both positions: logits (2, 4); context = 1 + sigmoid(4 - 2).
+    Row 0: causal sees only position 0 (context 1); non-causal logits (1/2, 1),
+    context 1 + sigmoid(1/2). Output = context / 2 in channel 0."""
+    x = np.array([[[1.0, 0, 0, 0], [2.0, 1, 0, 1]]])
+    W_q, W_o = np.eye(4), np.eye(4)
+    W_c = np.array([[1.0, 0, 0, 0]])
+    W_k = np.ones((4, 1))
+    W_v = np.array([[1.0], [0], [0], [0]])
+    W_g = np.zeros((4, 4))
+    res = O.gated_mla(x, W_q, W_c, W_k, W_v, W_g, W_o, 1, causal)
+    want = np.zeros((1, 2, 4))
+    want[0, 0, 0] = 0.5 * (1.0 if causal else 1.0 + _sig(0.5))
+    want[0, 1, 0] = 0.5 * (1.0 + _sig(2.0))
+    return res, want
+
+
+def test_gated_two_positions_causal():
+    res, want = _gated_two_positions(True)
+    np.testing.assert_allclose(res["output"], want, rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(res["latent_cache"], [[[1.0], [2.0]]])
+
+
+def test_gated_two_positions_non_causal():
+    res, want = _gated_two_positions(False)
+    np.testing.assert_allclose(res["output"], want, rtol=1e-14, atol=1e-15)
+
+
+def test_gated_heads_are_channel_blocks():
+    """Two heads of width 2 (scale 1/sqrt 2) own channels {0,1} and {2,3}.
+    W_q = I, C_j = x_j[0], K_j = C_j (1, 0, 0, 3), V_j = C_j (1, 1, 1, 1),
+    gate 1/2, W_o = I; x_0 = (1,0,0,0), x_1 = (2,0,0,1): C = (1, 2).
+    Causal row 1: head 0 logits 2 C / sqrt 2 -> context 1 + sigmoid(sqrt 2) in
+    channels 0, 1; head 1 logits 3 C / sqrt 2 -> 1 + sigmoid(3 / sqrt 2) in
+    channels 2, 3 (an interleaved head split mixes them)."""
+    x = np.array([[[1.0, 0, 0, 0], [2.0, 0, 0, 1]]])
+    W_c = np.array([[1.0, 0, 0, 0]])
+    W_k = np.array([[1.0], [0], [0], [3.0]])
+    W_v = np.ones((4, 1))
+    res = O.gated_mla(x, np.eye(4), W_c, W_k, W_v, np.zeros((4, 4)), np.eye(4), 2, True)
+    a, b = 0.5 * (1 + _sig(math.sqrt(2.0))), 0.5 * (1 + _sig(3 / math.sqrt(2.0)))
+    np.testing.assert_allclose(res["output"][0, 1], [a, a, b, b], rtol=1e-14)
+    np.testing.assert_allclose(res["output"][0, 0], [0.5] * 4, rtol=1e-14)
 
 
 def test_single_position_returns_latent_row():

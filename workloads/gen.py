@@ -307,8 +307,13 @@ def config5_prefill_bf16(seed=0):
 # the ferrox-core unit-test shape (docs.rs page, mla_absorbed.rs test)
 # --------------------------------------------------------------------------
 def xorshift32_stream(seed: int):
-    """xorshift32 (shifts 13, 17, 5) mapped to [-0.5, 0.5) in float32, as the
-    ferrox-core absorbed-vs-naive test draws its inputs."""
+    """Marsaglia's 32-bit xorshift generator ("Xorshift RNGs", Journal of
+    Statistical Software 8(14), 2003) with the shift triple (13, 17, 5): the
+    state x becomes x ^ (x << 13), then x ^ (x >> 17), then x ^ (x << 5)
+    (mod 2^32), and each new state is mapped to float32 as x / (2^32 - 1) - 1/2.
+    The ferrox-core absorbed-vs-naive test draws its inputs from this
+    generator; its page supplies the seed, the triple, the [-1/2, 1/2) mapping
+    and the draw order."""
     s = np.uint32(seed)
     umax = np.float32(4294967295.0)
     half = np.float32(0.5)
@@ -320,8 +325,10 @@ def xorshift32_stream(seed: int):
 
 
 def p2_tiny_case():
-    """Inputs of the ferrox-core test: H=3, nope=4, rope=2, v=5, kv_lora=6, seq=7.
-    Draw order: kv_b per head ([nope+v, kv_lora] row-major), latent, naive q."""
+    """Inputs at the ferrox-core test's shape (H=3, nope=4, rope=2, v=5,
+    kv_lora=6, seq=7), drawn from the xorshift32 stream above in the order the
+    page gives: every head's kv_b block ([nope+v, kv_lora], row-major), then
+    the latent rows, then the naive query."""
     H, nope, rope, v_dim, kv_lora, seq = 3, 4, 2, 5, 6, 7
     g = xorshift32_stream(0x9E37)
     kv_b = np.array([[next(g) for _ in range((nope + v_dim) * kv_lora)] for _ in range(H)],
