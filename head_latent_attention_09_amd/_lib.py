@@ -31,6 +31,9 @@ SIGNATURES = [
     ("mla_latent_decode_workspace", _sz, [_i, _i, _i, _i]),
     ("mla_latent_decode", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i,
                                _vp, _vp, _vp, _sz, _i, _vp, _vp]),
+    ("mla_latent_decode_noalloc_scratch_bytes", _sz, [_i, _i, _i, _i, _i]),
+    ("mla_latent_decode_noalloc", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i,
+                                       _vp, _vp, _i, _vp]),
     ("mla_latent_decode_up_v_workspace", _sz, [_i, _i, _i, _i]),
     ("mla_latent_decode_up_v", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _i, _i,
                                     _vp, _vp, _vp, _sz, _i, _vp, _vp]),
@@ -263,6 +266,35 @@ def latent_decode(q, cache, seq_lens, d_c, kq_scale, block_table=None, num_pages
         _ptr(q), _ptr(cache), _ptr(seq_lens), _ptr(block_table), B, H, d_c, d_r, stride, page_size,
         max_pages, num_pages, float(kq_scale), _dtype_code(q), _ptr(out), _ptr(lse),
         _ptr(ws), _ws_bytes(ws), num_workers, None if ev is None else ev[0], _stream()))
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 66 << 20
+
+
+def noalloc_scratch_bytes(batch, n_heads, d_c, dtype=torch.bfloat16, num_workers=0) -> int:
+    code = MLA_BF16 if dtype == torch.bfloat16 else MLA_F32
+    return int(lib.mla_latent_decode_noalloc_scratch_bytes(batch, n_heads, d_c, code, num_workers))
+
+
+def latent_decode_noalloc(q, cache, seq_lens, d_c, kq_scale, block_table=None, num_pages=None, num_workers=0,
+                          out=None, lse=None, want_lse=True):
+    """As latent_decode, through the library's allocation-free entry: no
+    workspace, the split plan and partials live in the library's fixed
+    per-device scratch (calls that overlap on one device race). The C call
+    allocates nothing; pass `out` (and `lse`) to keep this wrapper from
+    allocating them."""
+    B, H, W, stride, page_size, max_pages, num_pages, lse = _decode_inputs(
+        q, cache, seq_lens, d_c, block_table, num_pages, lse, want_lse)
+    d_r = W - d_c
+    if out is None:
+        out = torch.empty((B, H, d_c), dtype=q.dtype, device=q.device)
+    _like(q, out, "out", (B, H, d_c))
+    _on_gpu((q, "q"), (cache, "cache"), (seq_lens, "seq_lens"), (block_table, "block_table"), (out, "out"),
+            (lse, "lse"))
+    _check("mla_latent_decode_noalloc", lib.mla_latent_decode_noalloc(
+        _ptr(q), _ptr(cache), _ptr(seq_lens), _ptr(block_table), B, H, d_c, d_r, stride, page_size,
+        max_pages, num_pages, float(kq_scale), _dtype_code(q), _ptr(out), _ptr(lse), num_workers, _stream()))
     return out, lse
 
 

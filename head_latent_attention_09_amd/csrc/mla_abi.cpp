@@ -3,6 +3,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "mla_internal.h"
 
@@ -35,6 +36,34 @@ bool units_fit(int64_t rows, int64_t max_len) {
   return rows * ((max_len + 15) / 16 + SEG_COST) <= INT32_MAX / 2;
 }
 
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Fixed scratch of the allocation-free decode entry (mla_latent_decode_noalloc):
+// one array per device, held until the process ends. Host code never uses the
+// array's name as an address: the device address of each device's copy is
+// taken once, with that device current, by hipGetSymbolAddress and kept in
+// g_scratch_ptr.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null = not yet taken)
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -137,7 +166,7 @@ static int decode_call(const void* q, const void* latent_cache, const int32_t* s
                        int batch, int n_heads, int d_c, int d_r, int cache_stride, int page_size, int max_pages,
                        int num_pages, float kq_scale, int dtype, void* out_lat, float* lse, void* workspace,
                        size_t workspace_bytes, int num_workers, void* const* timing_events, void* stream,
-                       const void* w_uv, int d_v, void* v) {
+                       const void* w_uv, int d_v, void* v, bool use_scratch = false) {
   int st = attn_dims_check(batch, n_heads, d_c, d_r);
   if (st != MLA_OK) return st;
   if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
@@ -159,8 +188,17 @@ static int decode_call(const void* q, const void* latent_cache, const int32_t* s
   if (!units_fit(batch, cap)) return MLA_ERR_UNSUPPORTED;
   const int G = resolve_workers(num_workers);
   if (G <= 0) return G == 0 ? MLA_ERR_SHAPE : G;
+  int part_esize = 4;
+  if (use_scratch) {  // the library's fixed scratch: partials sized for the call's dtype
+    part_esize = elem_size(dtype);
+    if (plan_bytes(batch, G, n_heads, d_c, part_esize) > (size_t)MLA_NOALLOC_SCRATCH_BYTES)
+      return MLA_ERR_UNSUPPORTED;
+    st = scratch_address(&workspace);
+    if (st != MLA_OK) return st;
+    workspace_bytes = MLA_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace) return MLA_ERR_WORKSPACE;
-  size_t need = plan_bytes(batch, G, n_heads, d_c);
+  size_t need = plan_bytes(batch, G, n_heads, d_c, part_esize);
   if (w_uv) {  // out_lat in the workspace, after the plan
     out_lat = (char*)workspace + need;
     need += align256((size_t)batch * n_heads * d_c * sizeof(float));
@@ -186,6 +224,7 @@ static int decode_call(const void* q, const void* latent_cache, const int32_t* s
   c.out = out_lat;
   c.lse = lse;
   c.ws = workspace;
+  c.part_esize = part_esize;
   c.G = G;
   c.timing_events = timing_events;
   c.stream = (hipStream_t)stream;
@@ -202,6 +241,22 @@ int mla_latent_decode(const void* q, const void* latent_cache, const int32_t* se
   return decode_call(q, latent_cache, seq_lens, block_table, batch, n_heads, d_c, d_r, cache_stride, page_size,
                      max_pages, num_pages, kq_scale, dtype, out_lat, lse, workspace, workspace_bytes, num_workers,
                      timing_events, stream, nullptr, 0, nullptr);
+}
+
+int mla_latent_decode_noalloc(const void* q, const void* latent_cache, const int32_t* seq_lens,
+                              const int32_t* block_table, int batch, int n_heads, int d_c, int d_r, int cache_stride,
+                              int page_size, int max_pages, int num_pages, float kq_scale, int dtype, void* out_lat,
+                              float* lse, int num_workers, void* stream) {
+  return decode_call(q, latent_cache, seq_lens, block_table, batch, n_heads, d_c, d_r, cache_stride, page_size,
+                     max_pages, num_pages, kq_scale, dtype, out_lat, lse, nullptr, 0, num_workers, nullptr, stream,
+                     nullptr, 0, nullptr, true);
+}
+
+size_t mla_latent_decode_noalloc_scratch_bytes(int batch, int n_heads, int d_c, int dtype, int num_workers) {
+  if (batch < 0 || n_heads <= 0 || d_c <= 0 || !valid_dtype(dtype)) return 0;
+  int G = resolve_workers(num_workers);
+  if (G <= 0) return 0;
+  return plan_bytes(batch, G, n_heads, d_c, elem_size(dtype));
 }
 
 size_t mla_latent_decode_up_v_workspace(int batch, int n_heads, int d_c, int num_workers) {

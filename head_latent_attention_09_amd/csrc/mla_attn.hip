@@ -1252,7 +1252,7 @@ template <typename T>
 static int launch_attention_t(const AttnCall& c) {
   const bool mfma = use_mfma(c);
   const int tile = mfma ? mf::TILE : gn::TT;
-  Plan pl = plan_layout(c.ws, c.R, c.G, c.H, c.d_c, tile);
+  Plan pl = plan_layout(c.ws, c.R, c.G, c.H, c.d_c, tile, c.part_esize);
   constexpr int VEC = 16 / (int)sizeof(T);
   const bool vec_out = c.d_c % VEC == 0 && aligned16(c.out);
   // decode batches of up to SELF_MAX_R rows on the MFMA kernel plan inside

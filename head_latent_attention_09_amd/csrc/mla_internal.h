@@ -84,18 +84,21 @@ struct Plan {
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// workspace layout: cum | len | split | wrow | part_o | part_lse
-inline size_t plan_bytes(int64_t R, int G, int H, int d_c) {
+// workspace layout: cum | len | split | wrow | part_o | part_lse. The partial
+// outputs are stored in the call's dtype; `part_esize` is the element size
+// the region is sized for (4 for caller workspaces, whose size query takes no
+// dtype; the call's own size for the library's fixed scratch).
+inline size_t plan_bytes(int64_t R, int G, int H, int d_c, int part_esize = 4) {
   size_t b = align256(sizeof(int32_t) * (size_t)(R + 1));
   b += align256(sizeof(int32_t) * (size_t)R);
   b += align256(sizeof(int32_t) * (size_t)(4 + 4 * G));
   b += align256(sizeof(int32_t) * (size_t)G);
-  b += align256(sizeof(float) * (size_t)2 * G * H * d_c);
+  b += align256((size_t)part_esize * 2 * G * H * d_c);
   b += align256(sizeof(float) * (size_t)2 * G * H);
   return b;
 }
 
-inline Plan plan_layout(void* ws, int R, int G, int H, int d_c, int tile) {
+inline Plan plan_layout(void* ws, int R, int G, int H, int d_c, int tile, int part_esize = 4) {
   char* p = (char*)ws;
   Plan pl;
   pl.cum = (int32_t*)p;
@@ -107,7 +110,7 @@ inline Plan plan_layout(void* ws, int R, int G, int H, int d_c, int tile) {
   pl.wrow = (int32_t*)p;
   p += align256(sizeof(int32_t) * (size_t)G);
   pl.part_o = (float*)p;
-  p += align256(sizeof(float) * (size_t)2 * G * H * d_c);
+  p += align256((size_t)part_esize * 2 * G * H * d_c);
   pl.part_lse = (float*)p;
   pl.R = R;
   pl.G = G;
@@ -179,6 +182,7 @@ struct AttnCall {
   void* out;
   float* lse;
   void* ws;
+  int part_esize = 4;  // element size the workspace's partial-output region is sized for
   int G;
   void* const* timing_events;
   hipStream_t stream;

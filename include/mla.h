@@ -142,6 +142,40 @@ int mla_latent_decode(const void* q, const void* latent_cache,
                       int num_workers, void* const* timing_events, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Allocation-free absorbed decode, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Computes exactly what mla_latent_decode computes, with
+ * the same kernels and results, but takes no workspace: the split plan and
+ * the partial results live in a fixed scratch array inside the library, one
+ * per device (MLA_NOALLOC_SCRATCH_BYTES = 66 MiB, taken when the library's
+ * code is loaded on the device and held until the process ends). The call
+ * allocates nothing and calls no allocating routine.
+ *   Arguments as mla_latent_decode, without workspace / workspace_bytes /
+ *   timing_events.
+ *   Every call on a device shares that device's scratch: calls that may
+ *   overlap on one device (other streams, other threads) race and must be
+ *   serialised by the caller. Nothing in the scratch needs clearing between
+ *   calls: every value a kernel of the call reads is written earlier in the
+ *   same call.
+ *   Returns MLA_ERR_UNSUPPORTED, before any launch, when the call needs more
+ *   than the scratch holds: mla_latent_decode_noalloc_scratch_bytes(batch,
+ *   n_heads, d_c, dtype, num_workers) gives the need (bf16 at 256 workers,
+ *   128 heads, d_c = 512 takes about 64.3 MiB, which fits up to some two
+ *   hundred thousand sequences; fp32 needs twice the partial region).
+ * ------------------------------------------------------------------------- */
+#define MLA_NOALLOC_SCRATCH_BYTES (66u << 20)
+
+size_t mla_latent_decode_noalloc_scratch_bytes(int batch, int n_heads, int d_c, int dtype, int num_workers);
+
+int mla_latent_decode_noalloc(const void* q, const void* latent_cache,
+                              const int32_t* seq_lens, const int32_t* block_table,
+                              int batch, int n_heads, int d_c, int d_r,
+                              int cache_stride, int page_size, int max_pages, int num_pages,
+                              float kq_scale, int dtype,
+                              void* out_lat, float* lse,
+                              int num_workers, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Absorbed decode followed by the value up-projection, in one call (ferrox-
  * core module documentation: v[h] = wv_b[h] . out_lat[h]; the chain
  * mla_latent_decode -> mla_up_v without storing out_lat):

@@ -189,3 +189,23 @@ def test_workspace_formula():
         a256(4 * 8193) + a256(4 * 8192) + a256(4 * (4 + 4 * 256)) + a256(4 * 256) + a256(4 * 2 * 256 * 128 * 512)
         + a256(4 * 2 * 256 * 128))
     assert M.decode_workspace_bytes(-1, 4, 16, 8) == 0
+
+
+def test_noalloc_scratch_limit():
+    """The allocation-free decode sizes its need with the call's dtype and
+    refuses, before any HIP call, what the fixed scratch cannot hold."""
+    def a256(x):
+        return (x + 255) // 256 * 256
+    B, H, d_c, G = 64, 128, 512, 256
+    want = (a256(4 * (B + 1)) + a256(4 * B) + a256(4 * (4 + 4 * G)) + a256(4 * G) + a256(2 * 2 * G * H * d_c)
+            + a256(4 * 2 * G * H))
+    assert M.lib.mla_latent_decode_noalloc_scratch_bytes(B, H, d_c, M.MLA_BF16, G) == want
+    assert want <= M.NOALLOC_SCRATCH_BYTES
+    assert M.lib.mla_latent_decode_noalloc_scratch_bytes(B, H, d_c, M.MLA_F32, G) > M.NOALLOC_SCRATCH_BYTES
+    rc = M.lib.mla_latent_decode_noalloc(FAKE, FAKE, FAKE, None, B, H, d_c, 64, 16, 0, 0, 0, 0.1, M.MLA_F32,
+                                         FAKE, FAKE, G, None)
+    assert rc == -4
+    assert M.lib.mla_latent_decode_noalloc(FAKE, FAKE, FAKE, None, 0, H, d_c, 64, 16, 0, 0, 0, 0.1, M.MLA_BF16,
+                                           None, None, G, None) == 0
+    assert M.lib.mla_latent_decode_noalloc(FAKE, FAKE, None, None, 2, H, d_c, 64, 16, 0, 0, 0, 0.1, M.MLA_BF16,
+                                           FAKE, FAKE, G, None) == -1
