@@ -42,6 +42,8 @@ __all__ = [
     "mha_cache_values_per_token", "mla_cache_values_per_token", "cache_ratio",
     "notebook_head_blocks", "notebook_linear_absorbed", "notebook_linear_unabsorbed",
     "notebook_softmax_unabsorbed", "gated_mla",
+    "rms_norm", "rope", "latent_cache_rows", "append_rows", "mha_attention",
+    "full_absorbed_weights", "full_absorbed_decode", "training_form_decode",
 ]
 
 
@@ -388,3 +390,148 @@ def gated_mla(x, W_q, W_c, W_k, W_v, W_g, W_o, num_heads, causal):
     gate = 1.0 / (1.0 + np.exp(-(x @ _f64(W_g).T)))
     Y = (gate * Ot) @ _f64(W_o).T
     return {"output": Y, "latent_cache": C}
+
+
+# --------------------------------------------------------------------------
+# the step before the path: the new token's latent row ([tutorial] training
+# form c_i = x_i W_c and k_i's rope half x_i W_kr R_i, taken from x and not
+# from c; [ferrox] module doc: the cached latent is RMS-normed and the rope
+# key roped; [notebook] update-cache step: the new row is appended before the
+# query attends, so the token sees itself)
+# --------------------------------------------------------------------------
+def rms_norm(z, eps, gain=None):
+    """Root-mean-square normalisation over the last axis: z / sqrt(mean(z^2) + eps),
+    times `gain` when given. Pinned by: unit RMS of the result, invariance
+    under scaling z, brute-force sums."""
+    z = _f64(z)
+    r = z / np.sqrt(np.mean(z * z, axis=-1, keepdims=True) + eps)
+    return r if gain is None else r * _f64(gain)
+
+
+def rope(x, positions, base):
+    """Rotary position rotation of the last axis in interleaved pairs.
+
+    Pair i = (x[2i], x[2i+1]) turns by the angle p * base^(-2i/d) at position
+    p (the tutorial's R_i: a position-dependent rotation of the rope part).
+    positions broadcast against x's leading axes. Pinned by: identity at
+    position 0, norm of every pair kept, R(m) R(n) = R(m + n), dot products of
+    two rotated vectors depending only on the position difference, and
+    hand-computed quarter turns."""
+    x = _f64(x)
+    d = x.shape[-1]
+    if d == 0:
+        return x.copy()
+    assert d % 2 == 0, "rope width must be even"
+    i = np.arange(d // 2, dtype=np.float64)
+    theta = float(base) ** (-2.0 * i / d)
+    ang = np.asarray(positions, dtype=np.float64)[..., None] * theta
+    while ang.ndim < x.ndim:
+        ang = np.expand_dims(ang, -2)
+    c, s = np.cos(ang), np.sin(ang)
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    out[..., 1::2] = x[..., 0::2] * s + x[..., 1::2] * c
+    return out
+
+
+def latent_cache_rows(x, w_c, w_kr, positions, eps, base, gain=None):
+    """Cache rows of new tokens: [RMSNorm(W_c x) | RoPE(W_kr x, pos)].
+
+    x [N, d_model]; w_c [d_c, d_model] (c = W_c x, the tutorial's x W_c with
+    its matrix stored output-major); w_kr [d_r, d_model]; positions [N].
+    Returns rows [N, d_c + d_r]. Pinned by: brute-force sums of the two
+    projections, the rms_norm and rope pins, and the rope half depending on x
+    only through W_kr (not on c)."""
+    x = _f64(x)
+    c = rms_norm(x @ _f64(w_c).T, eps, gain)
+    k_pe = rope(x @ _f64(w_kr).T, positions, base)
+    return np.concatenate([c, k_pe], axis=1)
+
+
+def append_rows(cache, rows, seq_ids, positions, block_table=None):
+    """A copy of `cache` with row n written at sequence seq_ids[n], position
+    positions[n]: dense cache [B, S, W] at [seq, pos]; paged pool
+    [P, page, W] at page block_table[seq, pos // page], slot pos % page.
+    Every other element is unchanged. Pinned by: rows tagged with their own
+    (sequence, position) read back from where the block table says."""
+    out = np.array(cache, copy=True)
+    for n, (b, p) in enumerate(zip(seq_ids, positions)):
+        if block_table is None:
+            out[b, p] = rows[n]
+        else:
+            ps = out.shape[1]
+            out[block_table[b, p // ps], p % ps] = rows[n]
+    return out
+
+
+# --------------------------------------------------------------------------
+# standard per-head attention over expanded keys and values (the unabsorbed
+# prefill form: [tutorial] training form, k and v built per head from c;
+# [ferrox] test's naive branch)
+# --------------------------------------------------------------------------
+def mha_attention(q, k, v, scale, causal, rows=None):
+    """q [S_q, H, d_k], k [S_kv, H, d_k], v [S_kv, H, d_v]. Query i sees keys
+    t <= i + S_kv - S_q when causal (bottom-right alignment), else all.
+    Returns (out [len(rows), H, d_v], lse [len(rows), H]). Pinned by:
+    brute-force loops, and equality with the latent form when k, v are the
+    MLA expansion of a latent cache."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    S_q, H = q.shape[0], q.shape[1]
+    S_kv = k.shape[0]
+    rows = list(range(S_q) if rows is None else rows)
+    out = np.zeros((len(rows), H, v.shape[2]))
+    lse = np.full((len(rows), H), -math.inf)
+    for r, i in enumerate(rows):
+        n = causal_visible(i, S_q, S_kv) if causal else S_kv
+        for h in range(H):
+            out[r, h], lse[r, h] = attend_one_head(q[i, h], k[:, h], v[:, h], scale, n)
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# full absorption ([notebook] matrix absorption and head sum; [tutorial]
+# inference form c' W_qc W_kc^T)
+# --------------------------------------------------------------------------
+def full_absorbed_weights(w_uq, w_uk, w_uv, w_o):
+    """Absorbed weights of the query and output sides.
+
+    Per head: q_nope[h] = W_UQ[h] c' (W_UQ [H, d_nope, d_cq]), k_nope = W_UK[h] c
+    (W_UK [H, d_nope, d_c]), v = W_UV[h] c (W_UV [H, d_v, d_c]), and the layer
+    output sums W_O[:, h block] v[h] over heads (W_O [d_model, H d_v], head h
+    in columns h d_v .. (h+1) d_v - 1). Absorbing the query side gives
+        a_qk[h] = W_UK[h]^T W_UQ[h]            [d_c, d_cq]: q_abs[h] = a_qk[h] c'
+    (the notebook's W_aQK = W_uQ W_uK^T, transposed), and the output side
+        a_vo[:, h d_c .. (h+1) d_c] = W_O[:, h block] W_UV[h]    [d_model, H d_c]
+    (the notebook's W_aVO = W_uV W_O per head, transposed), so that
+    final = a_vo . concat_h(out_lat[h]) performs the head sum. Pinned by:
+    equality with the training form and the notebook's printed shapes."""
+    w_uq, w_uk, w_uv, w_o = _f64(w_uq), _f64(w_uk), _f64(w_uv), _f64(w_o)
+    H, d_v = w_uv.shape[0], w_uv.shape[1]
+    a_qk = np.stack([w_uk[h].T @ w_uq[h] for h in range(H)])
+    a_vo = np.concatenate([w_o[:, h * d_v:(h + 1) * d_v] @ w_uv[h] for h in range(H)], axis=1)
+    return a_qk, a_vo
+
+
+def full_absorbed_decode(c_q, q_pe, latent, d_c, a_qk, a_vo, scale, n_visible):
+    """One token through the fully absorbed layer: q_abs[h] = a_qk[h] c',
+    latent attention with [q_abs | q_pe] over the cache, then
+    final = a_vo . concat_h(out_lat[h]). Returns (final [d_model], out_lat [H, d_c])."""
+    c_q, a_qk = _f64(c_q), _f64(a_qk)
+    H = a_qk.shape[0]
+    q_abs = np.stack([a_qk[h] @ c_q for h in range(H)])
+    q = q_abs if q_pe is None else np.concatenate([q_abs, _f64(q_pe)], axis=1)
+    out_lat, _ = latent_attention(q, latent, d_c, scale, n_visible)
+    return _f64(a_vo) @ out_lat.reshape(-1), out_lat
+
+
+def training_form_decode(c_q, q_pe, latent, d_c, w_uq, w_uk, w_uv, w_o, scale, n_visible):
+    """The same token in the training form: per head q = [W_UQ[h] c' | q_pe[h]],
+    keys [W_UK[h] c_t | k_pe_t], values W_UV[h] c_t, softmax attention, then
+    final = sum_h W_O[:, h block] v[h]."""
+    q_nope = np.einsum("hij,j->hi", _f64(w_uq), _f64(c_q))
+    H = q_nope.shape[0]
+    qp = np.zeros((H, 0)) if q_pe is None else _f64(q_pe)
+    v, _ = mla_unabsorbed(q_nope, qp, latent, d_c, w_uk, w_uv, scale, n_visible)
+    d_v = v.shape[1]
+    w_o = _f64(w_o)
+    return sum(w_o[:, h * d_v:(h + 1) * d_v] @ v[h] for h in range(H))
