@@ -41,6 +41,21 @@ SIGNATURES = [
     ("mla_latent_prefill_causal", _i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                                        _vp, _vp, _vp, _sz, _i, _vp, _vp]),
     ("mla_lse_combine", _i, [_vp, _vp, _i, _i64, _i, _i, _i, _vp, _vp, _vp]),
+    ("mla_cache_append_workspace", _sz, [_i, _i, _i, _i, _i]),
+    ("mla_cache_append", _i, [_vp, _vp, _vp, _vp, _f, _f, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                              _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    ("mla_absorb_q_rope", _i, [_vp, _vp, _vp, _vp, _f, _vp, _i64, _i, _i, _i, _i, _i, _vp]),
+    ("mla_prefill_unabsorbed_workspace", _sz, [_i, _i, _i, _i, _i]),
+    ("mla_prefill_unabsorbed", _i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i,
+                                    _vp, _vp, _vp, _sz, _vp]),
+    ("mla_absorb_weights_workspace", _sz, [_i, _i, _i, _i, _i, _i]),
+    ("mla_absorb_weights", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    ("mla_absorb_q_full", _i, [_vp, _vp, _vp, _vp, _f, _vp, _i64, _i, _i, _i, _i, _i, _vp]),
+    ("mla_out_absorbed_workspace", _sz, [_i64, _i, _i, _i, _i]),
+    ("mla_out_absorbed", _i, [_vp, _vp, _vp, _i64, _i, _i, _i, _i, _vp, _sz, _vp]),
+    ("mla_gated_mla_workspace", _sz, [_i, _i, _i, _i, _i, _i, _i]),
+    ("mla_gated_mla", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
+                           _vp, _sz, _i, _vp]),
 ]
 
 
@@ -375,3 +390,224 @@ def lse_combine(o_parts, lse_parts, dtype=torch.float32, out=None, want_lse=True
     _check("mla_lse_combine", lib.mla_lse_combine(_ptr(o_parts), _ptr(lse_parts), P, R, H, d_c,
                                                   _dtype_code(out), _ptr(out), _ptr(lse), _stream()))
     return out, lse
+
+
+# ----------------------------------------------------------------------------
+# the steps around the core path
+# ----------------------------------------------------------------------------
+def _scratch(nbytes, ref):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=ref.device)
+
+
+def cache_append(x, w_c, w_kr, seq_ids, positions, cache, block_table=None, gain=None, eps=1e-6,
+                 rope_base=10000.0, n_seqs=None, num_pages=None):
+    """Write the new tokens' rows [RMSNorm(W_c x) | RoPE(W_kr x, pos)] into the
+    cache (dense [S, stride, d_c + d_r] or paged [P, page, d_c + d_r]) in place.
+    x [N, d_model], w_c [d_c, d_model], w_kr [d_r, d_model], seq_ids and
+    positions int32 [N]. Returns the cache."""
+    _ndim(x, "x", 2)
+    N, d_model = x.shape
+    _dtype_code(x)
+    _ndim(w_c, "w_c", 2)
+    d_c = w_c.shape[0]
+    _like(x, w_c, "w_c", (d_c, d_model))
+    _ndim(w_kr, "w_kr", 2)
+    d_r = w_kr.shape[0]
+    _like(x, w_kr, "w_kr", (d_r, d_model))
+    if gain is not None:
+        _like(x, gain, "gain", (d_c,))
+    _like(x, seq_ids, "seq_ids", (N,), dtype=torch.int32)
+    _like(x, positions, "positions", (N,), dtype=torch.int32)
+    _ndim(cache, "cache", 3)
+    _like(x, cache, "cache", (None, None, d_c + d_r))
+    if block_table is not None:
+        _ndim(block_table, "block_table", 2)
+        _like(x, block_table, "block_table", (None, None), dtype=torch.int32)
+        n_seqs = block_table.shape[0] if n_seqs is None else n_seqs
+        if not 0 <= n_seqs <= block_table.shape[0]:
+            raise ValueError(f"n_seqs = {n_seqs} must be in 0..{block_table.shape[0]} (block table rows)")
+        num_pages = cache.shape[0] if num_pages is None else num_pages
+        if not 0 < num_pages <= cache.shape[0]:
+            raise ValueError(f"num_pages = {num_pages} must be in 1..{cache.shape[0]}")
+        stride, page_size, max_pages = 0, cache.shape[1], block_table.shape[1]
+    else:
+        n_seqs = cache.shape[0] if n_seqs is None else n_seqs
+        if not 0 <= n_seqs <= cache.shape[0]:
+            raise ValueError(f"n_seqs = {n_seqs} must be in 0..{cache.shape[0]} (dense sequences)")
+        stride, page_size, max_pages, num_pages = cache.shape[1], 0, 0, 0
+    _on_gpu((x, "x"), (w_c, "w_c"), (w_kr, "w_kr"), (gain, "gain"), (seq_ids, "seq_ids"),
+            (positions, "positions"), (cache, "cache"), (block_table, "block_table"))
+    code = _dtype_code(x)
+    ws = _scratch(lib.mla_cache_append_workspace(N, d_model, d_c, d_r, code), x)
+    _check("mla_cache_append", lib.mla_cache_append(
+        _ptr(x), _ptr(w_c), _ptr(w_kr), _ptr(gain), float(eps), float(rope_base), _ptr(seq_ids), _ptr(positions),
+        _ptr(cache), _ptr(block_table), n_seqs, stride, page_size, max_pages, num_pages, N, d_model, d_c, d_r,
+        code, _ptr(ws), _ws_bytes(ws), _stream()))
+    return cache
+
+
+def absorb_q_rope(q_nope, q_pe, w_uk, positions, rope_base=10000.0, out=None):
+    """q[n,h,:d_c] = W_UK[h]^T q_nope[n,h]; q[n,h,d_c:] = RoPE(q_pe[n,h], positions[n])."""
+    _ndim(q_nope, "q_nope", 3)
+    N, H, d_nope = q_nope.shape
+    _dtype_code(q_nope)
+    _ndim(w_uk, "w_uk", 3)
+    d_c = w_uk.shape[2]
+    _like(q_nope, w_uk, "w_uk", (H, d_nope, d_c))
+    _ndim(q_pe, "q_pe", 3)
+    d_r = q_pe.shape[2]
+    _like(q_nope, q_pe, "q_pe", (N, H, d_r))
+    _like(q_nope, positions, "positions", (N,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((N, H, d_c + d_r), dtype=q_nope.dtype, device=q_nope.device)
+    _like(q_nope, out, "out", (N, H, d_c + d_r))
+    _on_gpu((q_nope, "q_nope"), (q_pe, "q_pe"), (w_uk, "w_uk"), (positions, "positions"), (out, "out"))
+    _check("mla_absorb_q_rope", lib.mla_absorb_q_rope(_ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(positions),
+                                                      float(rope_base), _ptr(out), N, H, d_nope, d_c, d_r,
+                                                      _dtype_code(q_nope), _stream()))
+    return out
+
+
+def prefill_unabsorbed(q_nope, q_pe, cache, w_uk, w_uv, kq_scale, out=None, lse=None, want_lse=True, workspace=None):
+    """Causal prefill in the expanded form: q_nope [B,S_q,H,d_nope], q_pe
+    [B,S_q,H,d_r], cache [B,S_kv,d_c+d_r], w_uk [H,d_nope,d_c], w_uv [H,d_v,d_c].
+    Returns (out [B,S_q,H,d_v], lse [B,S_q,H] or None)."""
+    _ndim(q_nope, "q_nope", 4)
+    B, S_q, H, d_nope = q_nope.shape
+    _dtype_code(q_nope)
+    _ndim(w_uk, "w_uk", 3)
+    d_c = w_uk.shape[2]
+    _like(q_nope, w_uk, "w_uk", (H, d_nope, d_c))
+    _ndim(w_uv, "w_uv", 3)
+    d_v = w_uv.shape[1]
+    _like(q_nope, w_uv, "w_uv", (H, d_v, d_c))
+    _ndim(cache, "cache", 3)
+    W = cache.shape[2]
+    d_r = W - d_c
+    if d_r < 0:
+        raise ValueError(f"cache rows ({W}) narrower than d_c ({d_c})")
+    _like(q_nope, cache, "cache", (B, None, W))
+    S_kv = cache.shape[1]
+    if d_r > 0:
+        _like(q_nope, q_pe, "q_pe", (B, S_q, H, d_r))
+    if out is None:
+        out = torch.empty((B, S_q, H, d_v), dtype=q_nope.dtype, device=q_nope.device)
+    _like(q_nope, out, "out", (B, S_q, H, d_v))
+    if lse is None and want_lse:
+        lse = torch.empty((B, S_q, H), dtype=torch.float32, device=q_nope.device)
+    if lse is not None:
+        _like(q_nope, lse, "lse", (B, S_q, H), dtype=torch.float32)
+    _on_gpu((q_nope, "q_nope"), (q_pe, "q_pe"), (cache, "cache"), (w_uk, "w_uk"), (w_uv, "w_uv"), (out, "out"),
+            (lse, "lse"))
+    nb = lib.mla_prefill_unabsorbed_workspace(B, S_kv, H, d_nope, d_v)
+    ws = _workspace(nb, q_nope, workspace)
+    _check("mla_prefill_unabsorbed", lib.mla_prefill_unabsorbed(
+        _ptr(q_nope), _ptr(q_pe) if d_r else None, _ptr(cache), _ptr(w_uk), _ptr(w_uv), B, S_q, S_kv, H, d_nope,
+        d_c, d_r, d_v, float(kq_scale), _dtype_code(q_nope), _ptr(out), _ptr(lse), _ptr(ws), _ws_bytes(ws),
+        _stream()))
+    return out, lse
+
+
+def prefill_unabsorbed_workspace_bytes(batch, s_kv, n_heads, d_nope=128, d_v=128) -> int:
+    return int(lib.mla_prefill_unabsorbed_workspace(batch, s_kv, n_heads, d_nope, d_v))
+
+
+def absorb_weights(w_uq, w_uk, w_uv, w_o):
+    """Absorbed weights: a_qk [H, d_c, d_cq] = W_UK[h]^T W_UQ[h];
+    a_vo [d_model, H d_c] with column block h = W_O[:, h block] W_UV[h]."""
+    _ndim(w_uq, "w_uq", 3)
+    H, d_nope, d_cq = w_uq.shape
+    _dtype_code(w_uq)
+    _ndim(w_uk, "w_uk", 3)
+    d_c = w_uk.shape[2]
+    _like(w_uq, w_uk, "w_uk", (H, d_nope, d_c))
+    _ndim(w_uv, "w_uv", 3)
+    d_v = w_uv.shape[1]
+    _like(w_uq, w_uv, "w_uv", (H, d_v, d_c))
+    _ndim(w_o, "w_o", 2)
+    d_model = w_o.shape[0]
+    _like(w_uq, w_o, "w_o", (d_model, H * d_v))
+    a_qk = torch.empty((H, d_c, d_cq), dtype=w_uq.dtype, device=w_uq.device)
+    a_vo = torch.empty((d_model, H * d_c), dtype=w_uq.dtype, device=w_uq.device)
+    _on_gpu((w_uq, "w_uq"), (w_uk, "w_uk"), (w_uv, "w_uv"), (w_o, "w_o"))
+    code = _dtype_code(w_uq)
+    ws = _scratch(lib.mla_absorb_weights_workspace(H, d_nope, d_cq, d_c, d_v, code), w_uq)
+    _check("mla_absorb_weights", lib.mla_absorb_weights(
+        _ptr(w_uq), _ptr(w_uk), _ptr(w_uv), _ptr(w_o), H, d_nope, d_cq, d_c, d_v, d_model, code, _ptr(a_qk),
+        _ptr(a_vo), _ptr(ws), _ws_bytes(ws), _stream()))
+    return a_qk, a_vo
+
+
+def absorb_q_full(c_q, q_pe, a_qk, positions=None, rope_base=10000.0, out=None):
+    """q[n,h,:d_c] = a_qk[h] c_q[n]; q[n,h,d_c:] = q_pe[n,h] (rotated at positions[n] if given)."""
+    _ndim(c_q, "c_q", 2)
+    N, d_cq = c_q.shape
+    _dtype_code(c_q)
+    _ndim(a_qk, "a_qk", 3)
+    H, d_c = a_qk.shape[0], a_qk.shape[1]
+    _like(c_q, a_qk, "a_qk", (H, d_c, d_cq))
+    d_r = 0
+    if q_pe is not None:
+        _ndim(q_pe, "q_pe", 3)
+        d_r = q_pe.shape[2]
+        _like(c_q, q_pe, "q_pe", (N, H, d_r))
+    if positions is not None:
+        _like(c_q, positions, "positions", (N,), dtype=torch.int32)
+    if out is None:
+        out = torch.empty((N, H, d_c + d_r), dtype=c_q.dtype, device=c_q.device)
+    _like(c_q, out, "out", (N, H, d_c + d_r))
+    _on_gpu((c_q, "c_q"), (q_pe, "q_pe"), (a_qk, "a_qk"), (positions, "positions"), (out, "out"))
+    _check("mla_absorb_q_full", lib.mla_absorb_q_full(_ptr(c_q), _ptr(q_pe), _ptr(a_qk), _ptr(positions),
+                                                      float(rope_base), _ptr(out), N, H, d_cq, d_c, d_r,
+                                                      _dtype_code(c_q), _stream()))
+    return out
+
+
+def out_absorbed(out_lat, a_vo, out=None, workspace=None):
+    """out[n,:] = a_vo . concat_h(out_lat[n,h,:]): out_lat [N,H,d_c], a_vo [d_model, H d_c]."""
+    _ndim(out_lat, "out_lat", 3)
+    N, H, d_c = out_lat.shape
+    _dtype_code(out_lat)
+    _ndim(a_vo, "a_vo", 2)
+    d_model = a_vo.shape[0]
+    _like(out_lat, a_vo, "a_vo", (d_model, H * d_c))
+    if out is None:
+        out = torch.empty((N, d_model), dtype=out_lat.dtype, device=out_lat.device)
+    _like(out_lat, out, "out", (N, d_model))
+    _on_gpu((out_lat, "out_lat"), (a_vo, "a_vo"), (out, "out"))
+    code = _dtype_code(out_lat)
+    ws = _workspace(lib.mla_out_absorbed_workspace(N, H, d_c, d_model, code), out_lat, workspace)
+    _check("mla_out_absorbed", lib.mla_out_absorbed(_ptr(out_lat), _ptr(a_vo), _ptr(out), N, H, d_c, d_model, code,
+                                                    _ptr(ws), _ws_bytes(ws), _stream()))
+    return out
+
+
+def gated_mla(x, w_q, w_c, w_k, w_v, w_g, w_o, num_heads, causal, out=None, latent_cache=None, num_workers=0,
+              workspace=None):
+    """Gated MLA layer: x [B,S,D]; w_q, w_g, w_o [D,D]; w_c [L,D]; w_k, w_v [D,L].
+    Returns dict(output [B,S,D], latent_cache [B,S,L])."""
+    _ndim(x, "x", 3)
+    B, S, D = x.shape
+    _dtype_code(x)
+    _ndim(w_c, "w_c", 2)
+    L = w_c.shape[0]
+    for t, name, shape in ((w_q, "w_q", (D, D)), (w_c, "w_c", (L, D)), (w_k, "w_k", (D, L)), (w_v, "w_v", (D, L)),
+                           (w_g, "w_g", (D, D)), (w_o, "w_o", (D, D))):
+        _like(x, t, name, shape)
+    if num_heads <= 0 or D % num_heads:
+        raise ValueError(f"d_model {D} is not divisible by num_heads {num_heads}")
+    if out is None:
+        out = torch.empty((B, S, D), dtype=x.dtype, device=x.device)
+    _like(x, out, "out", (B, S, D))
+    if latent_cache is None:
+        latent_cache = torch.empty((B, S, L), dtype=x.dtype, device=x.device)
+    _like(x, latent_cache, "latent_cache", (B, S, L))
+    _on_gpu((x, "x"), (w_q, "w_q"), (w_c, "w_c"), (w_k, "w_k"), (w_v, "w_v"), (w_g, "w_g"), (w_o, "w_o"),
+            (out, "out"), (latent_cache, "latent_cache"))
+    code = _dtype_code(x)
+    G = num_workers if num_workers > 0 else default_workers()
+    ws = _workspace(lib.mla_gated_mla_workspace(B, S, D, L, num_heads, code, G), x, workspace)
+    _check("mla_gated_mla", lib.mla_gated_mla(_ptr(x), _ptr(w_q), _ptr(w_c), _ptr(w_k), _ptr(w_v), _ptr(w_g),
+                                              _ptr(w_o), B, S, D, L, num_heads, 1 if causal else 0, code, _ptr(out),
+                                              _ptr(latent_cache), _ptr(ws), _ws_bytes(ws), G, _stream()))
+    return {"output": out, "latent_cache": latent_cache}

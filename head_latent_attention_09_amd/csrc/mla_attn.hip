@@ -24,6 +24,7 @@ namespace mla {
 // ===========================================================================
 __device__ __forceinline__ int row_len(const RowMap& m, int r) {
   if (m.mode == 2) {  // prefill, bottom-right causal alignment: t <= i + s_kv - s_q
+    if (m.non_causal) return m.s_kv;
     int i = r % m.s_q;
     long long n = (long long)i + 1 + m.s_kv - m.s_q;
     return n < 0 ? 0 : (n > m.s_kv ? m.s_kv : (int)n);

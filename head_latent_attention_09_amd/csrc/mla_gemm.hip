@@ -578,7 +578,7 @@ int launch_absorb(const void* q_nope, const void* q_pe, const void* w_uk, void* 
   }
   int st = dtype == MLA_BF16 ? run_generic<bf16, false>(q_nope, w_uk, q, N, H, d_nope, d_c, ldo, s)
                              : run_generic<float, false>(q_nope, w_uk, q, N, H, d_nope, d_c, ldo, s);
-  if (st != MLA_OK || d_r == 0) return st;
+  if (st != MLA_OK || d_r == 0 || !q_pe) return st;  // no q_pe: the tail is written elsewhere
   const int64_t rows = N * H;
   const int64_t blocks = (rows * d_r + 255) / 256;
   if (dtype == MLA_BF16)

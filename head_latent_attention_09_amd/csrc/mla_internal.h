@@ -163,6 +163,7 @@ __device__ __forceinline__ bool plan_segment(int c0, int c1, int cost, int t_beg
 struct RowMap {
   int mode;            // 0 = decode dense, 1 = decode paged, 2 = prefill
   int s_q, s_kv;       // prefill
+  int non_causal;      // prefill: every query sees all s_kv positions (no mask)
   int cache_stride;    // dense rows per sequence
   int page_size, max_pages, num_pages;
   const int32_t* block_table;
@@ -206,5 +207,70 @@ int launch_up_v(const void* lat, const void* w_uv, void* out, int64_t N, int H, 
 bool upv_merge_fits(int d_c, int d_v, const void* w_uv, const void* v);
 int launch_upv_merge(const Plan& pl, int R, int H, const void* lat, const void* w_uv, void* v, float* lse,
                      hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// argument helpers shared by the C ABI sources
+// ---------------------------------------------------------------------------
+inline int abi_esize(int dtype) { return dtype == MLA_BF16 ? 2 : 4; }
+inline bool abi_dtype_ok(int dtype) { return dtype == MLA_F32 || dtype == MLA_BF16; }
+inline bool abi_aligned(const void* p, int a) { return ((uintptr_t)p % (uintptr_t)a) == 0; }
+
+// ---------------------------------------------------------------------------
+// dense products and row kernels (mla_dense.hip)
+// ---------------------------------------------------------------------------
+// C[batch][split][m][n] = sum_k A[batch][m][k] B[batch][n][k] (row strides lda,
+// ldb, ldc in elements; batch strides may be 0). bf16 inputs on the MFMA path
+// need K a multiple of 64 and 16-byte aligned rows; anything else runs the
+// generic kernel (one split). out_f32: fp32 output (split-K partials at
+// c_split apart), else the output has the inputs' dtype (one split).
+struct GemmDesc {
+  const void* A;
+  const void* B;
+  void* C;
+  int64_t lda, ldb, ldc;
+  int64_t a_batch, b_batch, c_batch, c_split;
+  int M, N, K, batch;
+  int splits;
+  int dtype;
+  bool out_f32;
+};
+bool gemm_nt_mfma_ok(const GemmDesc& g);
+int gemm_nt_splits(const GemmDesc& g, int cus);
+int launch_gemm_nt(const GemmDesc& g, hipStream_t s);
+int launch_splitk_reduce(const float* P, int splits, int64_t split_stride, int64_t ldp, void* C, int64_t ldc, int M,
+                         int N, int dtype, hipStream_t s);
+int launch_transpose(const void* in, void* out, int rows, int cols, int batch, int64_t in_batch, int64_t out_batch,
+                     int dtype, hipStream_t s);
+int launch_cache_rows(const float* P, int splits, int64_t split_stride, const void* gain, float eps, float rope_base,
+                      const int32_t* seq_ids, const int32_t* positions, void* cache, const RowMap& map, int n_seqs,
+                      int n_tokens, int d_c, int d_r, int dtype, hipStream_t s);
+// dst[n, h, col0 + j] = rotation of src[n, h, j] at positions[n] (positions
+// NULL: a plain copy)
+int launch_rope_rows(const void* src, void* dst, const int32_t* positions, int64_t rows, int H, int d_r, int ldd,
+                     int col0, float rope_base, int dtype, hipStream_t s);
+// x[i] *= sigmoid(g[i]) for i < n
+int launch_gate(void* x, const void* g, int64_t n, int dtype, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// standard per-head attention (mla_flash.hip): bf16, d_nope = d_v = 128,
+// d_r 0 or 64 (rope key shared by all heads). Element (row, head, dim) of a
+// tensor sits at base + row * X_row + head * X_head + dim; rows are
+// batch * S + position.
+// ---------------------------------------------------------------------------
+struct FlashDesc {
+  const void* q;  int64_t q_row, q_head;    // [.., 128] nope (or whole) query
+  const void* qr; int64_t qr_row, qr_head;  // [.., d_r] rope query (d_r > 0)
+  const void* k;  int64_t k_row, k_head;    // [.., 128] keys (nope part)
+  const void* kr; int64_t kr_row;           // [.., d_r] shared rope key (d_r > 0)
+  const void* v;  int64_t v_row, v_head;    // [.., 128]
+  void* o;        int64_t o_row, o_head;    // [.., 128] output
+  float* lse;                               // [B * S_q, H] or null
+  const void* gate; int64_t g_row, g_head;  // output times sigmoid(gate), or null
+  int B, S_q, S_kv, H, d_r;
+  float scale;
+  bool causal;
+};
+bool flash_fits(int d_nope, int d_r, int d_v);
+int launch_flash(const FlashDesc& f, hipStream_t s);
 
 }  // namespace mla

@@ -245,6 +245,142 @@ int mla_lse_combine(const float* o_parts, const float* lse_parts, int n_parts,
                     int64_t rows, int n_heads, int d_c, int dtype,
                     void* out, float* lse, void* stream);
 
+/* ===========================================================================
+ * The steps around the core path
+ * ========================================================================= */
+
+/* ---------------------------------------------------------------------------
+ * Fused cache append: the new tokens' latent rows written straight into the
+ * cache. Per token n (MLA_tutorial formula.md Part 3, training form: the
+ * latent c = x W_c and the rope key x W_kr R_i, taken from x and not from c;
+ * ferrox-core module documentation: the cached latent is RMS-normed and the
+ * rope key roped; notebook MLA_RoPE-less.ipynb, cache update: the new row is
+ * appended before the query attends, so the token sees itself):
+ *   z   = W_c x_n                      (w_c  [d_c, d_model], a row per latent dim)
+ *   c   = z / sqrt(mean(z^2) + eps) * gain      (gain [d_c] or NULL = 1)
+ *   kr  = W_kr x_n                     (w_kr [d_r, d_model])
+ *   k_pe = kr with pair (2i, 2i+1) turned by positions[n] * rope_base^(-2i/d_r)
+ *   row [c | k_pe] written at sequence seq_ids[n], position positions[n]:
+ *     dense  (block_table NULL): latent_cache[seq][pos], [n_seqs, cache_stride, d_c + d_r];
+ *     paged: pool page block_table[seq][pos / page_size], slot pos % page_size.
+ * x [n_tokens, d_model]; seq_ids, positions [n_tokens] int32 DEVICE memory.
+ * latent_cache is the one buffer written (only the addressed rows); a token
+ * whose sequence, position or page falls outside the cache is skipped.
+ * Rotation angles are formed in double precision on the device.
+ * workspace: mla_cache_append_workspace(n_tokens, d_model, d_c, d_r, dtype)
+ *   bytes (fp32 partial projections).
+ * Status: MLA_ERR_SCALE for eps < 0, a non-finite eps or rope_base <= 0.
+ * Limits: d_model <= 65536, d_c <= 4096, d_r <= 1024 and even.
+ * ------------------------------------------------------------------------- */
+size_t mla_cache_append_workspace(int n_tokens, int d_model, int d_c, int d_r, int dtype);
+
+int mla_cache_append(const void* x, const void* w_c, const void* w_kr, const void* gain,
+                     float eps, float rope_base,
+                     const int32_t* seq_ids, const int32_t* positions,
+                     void* latent_cache, const int32_t* block_table,
+                     int n_seqs, int cache_stride, int page_size, int max_pages, int num_pages,
+                     int n_tokens, int d_model, int d_c, int d_r, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Query absorption with the query's rope part rotated on the way (the query
+ * side of the fused append; MLA_tutorial inference form: q = [c' W_qc W_kc^T,
+ * c' W_qr R_i]):
+ *   q[n,h,:d_c] as mla_absorb_q;  q[n,h,d_c:] = q_pe[n,h,:] turned by
+ *   positions[n] as in mla_cache_append (same angles).
+ * positions [n_tokens] int32 DEVICE memory. d_r > 0 and even.
+ * ------------------------------------------------------------------------- */
+int mla_absorb_q_rope(const void* q_nope, const void* q_pe, const void* w_uk,
+                      const int32_t* positions, float rope_base, void* q,
+                      int64_t n_tokens, int n_heads, int d_nope, int d_c, int d_r,
+                      int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Unabsorbed causal prefill: keys and values expanded per head, then
+ * standard softmax attention (MLA_tutorial formula.md Part 3, training form:
+ * k[t,h] = [W_UK[h] c_t | k_pe_t], v[t,h] = W_UV[h] c_t, the rope key shared
+ * by all heads; its closing remarks: absorption widens the head to d_c + d_r,
+ * so the expanded form is the cheaper one where the work is compute-bound).
+ *   out[b,i,h,:] = sum_t softmax_t(([q_nope | q_pe][b,i,h] . k[b,t,h]) kq_scale) v[b,t,h]
+ * over t <= i + s_kv - s_q (bottom-right causal alignment), i.e. the same
+ * result as mla_absorb_q -> mla_latent_prefill_causal -> mla_up_v.
+ * q_nope [batch, s_q, n_heads, d_nope], q_pe [batch, s_q, n_heads, d_r];
+ * latent_cache [batch, s_kv, d_c + d_r]; w_uk [n_heads, d_nope, d_c];
+ * w_uv [n_heads, d_v, d_c]; out [batch, s_q, n_heads, d_v]; lse
+ * [batch, s_q, n_heads] fp32 or NULL (queries that see nothing: 0, -inf).
+ * workspace: mla_prefill_unabsorbed_workspace(batch, s_kv, n_heads, d_nope,
+ *   d_v) bytes (the expanded keys and values).
+ * Supported: bf16, d_nope = d_v = 128, d_r 0 or 64, d_c a multiple of 64 up
+ * to 4096, 16-byte aligned tensors; anything else is MLA_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+size_t mla_prefill_unabsorbed_workspace(int batch, int s_kv, int n_heads, int d_nope, int d_v);
+
+int mla_prefill_unabsorbed(const void* q_nope, const void* q_pe, const void* latent_cache,
+                           const void* w_uk, const void* w_uv,
+                           int batch, int s_q, int s_kv, int n_heads, int d_nope, int d_c, int d_r,
+                           int d_v, float kq_scale, int dtype, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Full absorption (notebook MLA_RoPE-less.ipynb: matrix absorption and the
+ * sum over heads; MLA_tutorial inference form: c' W_qc W_kc^T).
+ * Weights: w_uq [n_heads, d_nope, d_cq] (q_nope[h] = W_UQ[h] c', c' the
+ * query latent), w_uk [n_heads, d_nope, d_c], w_uv [n_heads, d_v, d_c],
+ * w_o [d_model, n_heads * d_v] (layer output = sum_h W_O[:, h block] v[h]).
+ * mla_absorb_weights writes (once per weight set):
+ *   a_qk [n_heads, d_c, d_cq],   a_qk[h] = W_UK[h]^T W_UQ[h]
+ *   a_vo [d_model, n_heads * d_c], columns h*d_c.. = W_O[:, h block] W_UV[h]
+ * workspace: mla_absorb_weights_workspace(...) bytes (transposed copies).
+ * ------------------------------------------------------------------------- */
+size_t mla_absorb_weights_workspace(int n_heads, int d_nope, int d_cq, int d_c, int d_v, int dtype);
+
+int mla_absorb_weights(const void* w_uq, const void* w_uk, const void* w_uv, const void* w_o,
+                       int n_heads, int d_nope, int d_cq, int d_c, int d_v, int d_model, int dtype,
+                       void* a_qk, void* a_vo, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Absorbed query straight from the query latent:
+ *   q[n,h,:d_c] = a_qk[h] c_q[n];  q[n,h,d_c:] = q_pe[n,h,:], turned by
+ *   positions[n] as in mla_absorb_q_rope when positions is not NULL.
+ * c_q [n_tokens, d_cq]; q [n_tokens, n_heads, d_c + d_r]. */
+int mla_absorb_q_full(const void* c_q, const void* q_pe, const void* a_qk,
+                      const int32_t* positions, float rope_base, void* q,
+                      int64_t n_tokens, int n_heads, int d_cq, int d_c, int d_r, int dtype, void* stream);
+
+/* Layer output straight from the latent attention output, summed over heads:
+ *   out[n,:] = a_vo . concat_h(out_lat[n,h,:])   (the notebook's adding trick)
+ * out_lat [n_tokens, n_heads, d_c]; out [n_tokens, d_model].
+ * workspace: mla_out_absorbed_workspace(...) bytes (fp32 split partials). */
+size_t mla_out_absorbed_workspace(int64_t n_tokens, int n_heads, int d_c, int d_model, int dtype);
+
+int mla_out_absorbed(const void* out_lat, const void* a_vo, void* out,
+                     int64_t n_tokens, int n_heads, int d_c, int d_model, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Gated MLA (tensortonic "Kimi K3 step 2: Gated MLA", problem statement):
+ *   Q = X W_q^T, C = X W_c^T, K = C W_k^T, V = C W_v^T; per head of width
+ *   D_h = d_model / n_heads: A = softmax(Q K^T / sqrt(D_h) + M), M masking
+ *   later positions when causal != 0; O~ = heads side by side;
+ *   Y = [sigmoid(X W_g^T) * O~] W_o^T.
+ * x [batch, seq, d_model]; w_q, w_g, w_o [d_model, d_model]; w_c [latent,
+ * d_model]; w_k, w_v [d_model, latent]. Outputs: out [batch, seq, d_model]
+ * and latent_cache [batch, seq, latent] (= C). No positional encoding.
+ * bf16 with D_h = 128 runs per-head attention over the expanded keys and
+ * values; every other case runs the absorbed form (q_abs[h] = W_k[h]^T q[h],
+ * latent attention over C with C as the value, then W_v[h]) through the
+ * latent-attention kernels. num_workers as mla_latent_decode (absorbed form).
+ * workspace: mla_gated_mla_workspace(batch, seq, d_model, latent, n_heads,
+ *   dtype, num_workers) bytes.
+ * Limits: d_model divisible by n_heads, d_model <= 65536, latent <= 1024.
+ * ------------------------------------------------------------------------- */
+size_t mla_gated_mla_workspace(int batch, int seq, int d_model, int latent, int n_heads, int dtype,
+                               int num_workers);
+
+int mla_gated_mla(const void* x, const void* w_q, const void* w_c, const void* w_k, const void* w_v,
+                  const void* w_g, const void* w_o, int batch, int seq, int d_model, int latent,
+                  int n_heads, int causal, int dtype, void* out, void* latent_cache,
+                  void* workspace, size_t workspace_bytes, int num_workers, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

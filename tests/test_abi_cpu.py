@@ -209,3 +209,63 @@ def test_noalloc_scratch_limit():
                                            None, None, G, None) == 0
     assert M.lib.mla_latent_decode_noalloc(FAKE, FAKE, None, None, 2, H, d_c, 64, 16, 0, 0, 0, 0.1, M.MLA_BF16,
                                            FAKE, FAKE, G, None) == -1
+
+
+def test_next_entries_validation():
+    """Argument errors of the entries around the core path, all before any launch."""
+    L = M.lib
+    # cache append: dtype, sizes, scale-like arguments, NULLs, alignment, workspace
+    def app(**kw):
+        a = dict(x=FAKE, wc=FAKE, wk=FAKE, gain=None, eps=1e-6, base=1e4, seq=FAKE, pos=FAKE, cache=FAKE, table=None,
+                 n_seqs=2, stride=16, page=0, max_pages=0, num_pages=0, N=3, dm=64, dc=16, dr=4, dtype=M.MLA_BF16,
+                 ws=None, wsb=0)
+        a.update(kw)
+        return L.mla_cache_append(a["x"], a["wc"], a["wk"], a["gain"], a["eps"], a["base"], a["seq"], a["pos"],
+                                  a["cache"], a["table"], a["n_seqs"], a["stride"], a["page"], a["max_pages"],
+                                  a["num_pages"], a["N"], a["dm"], a["dc"], a["dr"], a["dtype"], a["ws"], a["wsb"], None)
+    assert app(dtype=3) == -3 and app(dr=3) == -2 and app(dm=0) == -2 and app(dm=70000) == -4
+    assert app(eps=-1.0) == -7 and app(base=0.0) == -7 and app(eps=math.nan) == -7
+    assert app(x=None) == -1 and app(pos=None) == -1 and app(wk=None) == -1
+    assert app(cache=ODD) == -6 and app(seq=FAKE + 2) == -6
+    assert app(table=FAKE, page=0, max_pages=4, num_pages=4) == -2 and app(stride=0) == -2
+    assert app() == -5                                        # no workspace
+    need = L.mla_cache_append_workspace(3, 64, 16, 4, M.MLA_BF16)
+    assert need >= 3 * 20 * 4 and app(ws=FAKE, wsb=need - 1) == -5
+    assert app(N=0) == 0 and app(N=0, x=None, wc=None, wk=None, seq=None, pos=None, cache=None) == 0
+    # absorb with rope
+    def arope(**kw):
+        a = dict(qn=FAKE, qp=FAKE, w=FAKE, pos=FAKE, base=1e4, q=FAKE, N=4, H=2, dn=8, dc=16, dr=4, dtype=M.MLA_BF16)
+        a.update(kw)
+        return L.mla_absorb_q_rope(a["qn"], a["qp"], a["w"], a["pos"], a["base"], a["q"], a["N"], a["H"], a["dn"],
+                                   a["dc"], a["dr"], a["dtype"], None)
+    assert arope(dr=0) == -2 and arope(dr=3) == -2 and arope(pos=None) == -1 and arope(base=-1.0) == -7
+    assert arope(N=0) == 0
+    # unabsorbed prefill: only bf16 with d_nope = d_v = 128 and d_r 0 / 64
+    def pu(**kw):
+        a = dict(qn=FAKE, qp=FAKE, cache=FAKE, wuk=FAKE, wuv=FAKE, B=1, Sq=8, Skv=8, H=2, dn=128, dc=512, dr=64,
+                 dv=128, scale=0.1, dtype=M.MLA_BF16, out=FAKE, ws=None, wsb=0)
+        a.update(kw)
+        return L.mla_prefill_unabsorbed(a["qn"], a["qp"], a["cache"], a["wuk"], a["wuv"], a["B"], a["Sq"], a["Skv"],
+                                        a["H"], a["dn"], a["dc"], a["dr"], a["dv"], a["scale"], a["dtype"], a["out"],
+                                        None, a["ws"], a["wsb"], None)
+    assert pu(dtype=M.MLA_F32) == -4 and pu(dn=64) == -4 and pu(dr=32) == -4 and pu(dc=500) == -4
+    assert pu(scale=math.inf) == -7 and pu(qp=None) == -1 and pu(out=FAKE + 8) == -6 and pu() == -5
+    assert pu(dr=0, qp=None, ws=None) == -5 and pu(B=0) == 0
+    assert L.mla_prefill_unabsorbed_workspace(2, 4096, 128, 128, 128) == (2 * 4096 * 128 * 256 * 2 + 255) // 256 * 256 + 256
+    # full absorption
+    assert L.mla_absorb_weights(FAKE, FAKE, FAKE, None, 2, 8, 16, 16, 8, 32, M.MLA_F32, FAKE, FAKE, FAKE, 1 << 30,
+                                None) == -1
+    assert L.mla_absorb_weights(FAKE, FAKE, FAKE, FAKE, 2, 8, 16, 16, 8, 32, M.MLA_F32, FAKE, FAKE, None, 0,
+                                None) == -5
+    assert L.mla_absorb_q_full(FAKE, None, FAKE, None, 1e4, FAKE, 4, 2, 16, 16, 4, M.MLA_F32, None) == -1
+    assert L.mla_absorb_q_full(FAKE, FAKE, FAKE, FAKE, 0.0, FAKE, 4, 2, 16, 16, 4, M.MLA_F32, None) == -7
+    assert L.mla_out_absorbed(FAKE, FAKE, FAKE, 4, 2, 16, 32, M.MLA_F32, None, 0, None) == -5
+    assert L.mla_out_absorbed(FAKE, FAKE, FAKE, 0, 2, 16, 32, M.MLA_F32, None, 0, None) == 0
+    # gated
+    def gm(**kw):
+        a = dict(B=1, S=4, D=8, L=2, H=2, causal=1, dtype=M.MLA_F32, ws=None, wsb=0)
+        a.update(kw)
+        return L.mla_gated_mla(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["S"], a["D"], a["L"], a["H"],
+                               a["causal"], a["dtype"], FAKE, FAKE, a["ws"], a["wsb"], 4, None)
+    assert gm(H=3) == -2 and gm(L=2000) == -4 and gm(dtype=7) == -3 and gm() == -5 and gm(S=0) == 0
+    assert L.mla_gated_mla_workspace(1, 4, 8, 2, 3, M.MLA_F32, 4) == 0
