@@ -14,12 +14,18 @@ Prints ONE JSON line. `value` is latent head-tokens attended per second
 (B*H*seq per step). `roofline` is for the dominant kernel (the latent
 attention kernel), timed with two HIP events passed with its launch on its own
 stream (they take the start and end of its dispatch) on every n-th timed step
-(--event-every, default 5).
+(--event-every, default 5); its algorithmic bytes are the cache read once, the
+absorbed queries and the latent output.
 `entry_points_ms` gives each entry point's own time (median and min over
 blocks of back-to-back calls, run before the warm-up steps). `cpu_baseline` times the fp64 CPU oracle on a
 bounded sample of the same workload on this host.
+`workloads` holds the other measured workloads, each with its own roofline:
+the ragged paged decode (B=128, lengths U[1, 32768], 64-position pages), the
+causal prefill B=2 S=4096 H=128 in both forms (absorbed chain and expanded
+per-head form), the fused cache append, full absorption, and the gated MLA
+layer (--headline-only skips them).
 
-    python bench.py [--steps K] [--warmup W] [--prefill] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -59,7 +65,8 @@ def parse():
                    help="record the attention kernel's timing events on every n-th timed step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
-    p.add_argument("--prefill", action="store_true", help="also time the causal-prefill chain (config 5)")
+    p.add_argument("--headline-only", action="store_true", help="skip the other workloads")
+    p.add_argument("--only", default="", help="comma-separated subset of the other workloads")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
@@ -213,7 +220,7 @@ def main():
 
     tokens = B * H * S
     value = tokens / (ms_step / 1e3)
-    alg_bytes = B * S * W * ESIZE + B * H * W * ESIZE          # latent cache + absorbed queries
+    alg_bytes = B * S * W * ESIZE + B * H * W * ESIZE + B * H * D_C * ESIZE   # cache + queries + latent output
     alg_flop = B * S * H * (2 * W + 2 * D_C)                   # QK (576) + PV (512) per head-position
     achieved = alg_bytes / (attn_avg / 1e3) / 1e9
     traffic = traffic_from_profile(alg_bytes)
@@ -245,10 +252,13 @@ def main():
         "wall_s_timed": round(wall, 3),
         "entry_points_ms": entry,
     }
-    if args.prefill:
-        line["prefill"] = bench_prefill(M, G, torch, dev, args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    if not args.headline_only:
+        del sets, q0, cache0, ws, ws_two
+        torch.cuda.empty_cache()
+        import bench_workloads as BW
+        line["workloads"] = BW.run_all(M, G, torch, dev, args, time_entry)
     print(json.dumps(line), flush=True)
 
 
@@ -269,66 +279,6 @@ def time_entry(torch, stream, call, per_block=20, blocks=5):
         res.append(e0.elapsed_time(e1) / per_block)
     return {"median": round(float(np.median(res)), 5), "min": round(float(np.min(res)), 5),
             "calls": per_block * blocks}
-
-
-def bench_prefill(M, G, torch, dev, args):
-    """Causal prefill chain of config 5: absorb -> prefill attention -> up_v."""
-    c = G.config5_prefill_bf16(0)
-
-    def to_dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    Bp, Sp, Hp = c.B, c.S_q, c.H
-    qn = to_dev(c.q_nope).reshape(Bp * Sp, Hp, -1)
-    qp = to_dev(c.q_pe).reshape(Bp * Sp, Hp, -1)
-    wuk, wuv, cache = to_dev(c.w_uk), to_dev(c.w_uv), to_dev(c.cache)
-    q = torch.empty((Bp * Sp, Hp, c.W), dtype=torch.bfloat16, device=dev)
-    out = torch.empty((Bp, Sp, Hp, c.d_c), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((Bp, Sp, Hp), dtype=torch.float32, device=dev)
-    v = torch.empty((Bp * Sp, Hp, c.d_v), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(M.prefill_workspace_bytes(Bp, Sp, Hp, c.d_c, 0), dtype=torch.uint8, device=dev)
-    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-
-    def step(e=None):
-        M.absorb_q(qn, qp, wuk, out=q)
-        M.latent_prefill_causal(q.view(Bp, Sp, Hp, -1), cache, c.d_c, c.kq_scale, out=out, lse=lse,
-                                workspace=ws, timing_events=e)
-        M.up_v(out.view(Bp * Sp, Hp, -1), wuv, out=v)
-
-    steps = max(3, args.steps // 10)
-    for _ in range(2):
-        step(ev)
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    attn = []
-    t0.record()
-    for _ in range(steps):
-        e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-        e[0].record(); e[1].record()
-        step(e)
-        attn.append(e)
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in attn]))
-    stream = torch.cuda.current_stream()
-    entry = {
-        "absorb_q": time_entry(torch, stream, lambda i: M.absorb_q(qn, qp, wuk, out=q), per_block=3, blocks=3),
-        "latent_prefill_causal": time_entry(
-            torch, stream, lambda i: M.latent_prefill_causal(q.view(Bp, Sp, Hp, -1), cache, c.d_c, c.kq_scale,
-                                                             out=out, lse=lse, workspace=ws),
-            per_block=3, blocks=3),
-        "up_v": time_entry(torch, stream, lambda i: M.up_v(out.view(Bp * Sp, Hp, -1), wuv, out=v),
-                           per_block=3, blocks=3),
-    }
-    pairs = Bp * Hp * Sp * (Sp + 1) // 2
-    flop = pairs * (2 * c.W + 2 * c.d_c)
-    return {"workload": "causal prefill B=2 S=4096 H=128 (absorb + attention + up_v)",
-            "ms_per_step": round(ms, 4), "latent_tokens_per_s": round(pairs / (ms / 1e3), 1),
-            "attention_ms": round(attn_ms, 4),
-            "attention_mfma_tflops": round(flop / (attn_ms / 1e3) / 1e12, 1),
-            "attention_mfma_frac": round(flop / (attn_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "entry_points_ms": entry}
 
 
 if __name__ == "__main__":

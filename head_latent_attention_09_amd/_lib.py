@@ -400,7 +400,7 @@ def _scratch(nbytes, ref):
 
 
 def cache_append(x, w_c, w_kr, seq_ids, positions, cache, block_table=None, gain=None, eps=1e-6,
-                 rope_base=10000.0, n_seqs=None, num_pages=None):
+                 rope_base=10000.0, n_seqs=None, num_pages=None, workspace=None):
     """Write the new tokens' rows [RMSNorm(W_c x) | RoPE(W_kr x, pos)] into the
     cache (dense [S, stride, d_c + d_r] or paged [P, page, d_c + d_r]) in place.
     x [N, d_model], w_c [d_c, d_model], w_kr [d_r, d_model], seq_ids and
@@ -438,7 +438,7 @@ def cache_append(x, w_c, w_kr, seq_ids, positions, cache, block_table=None, gain
     _on_gpu((x, "x"), (w_c, "w_c"), (w_kr, "w_kr"), (gain, "gain"), (seq_ids, "seq_ids"),
             (positions, "positions"), (cache, "cache"), (block_table, "block_table"))
     code = _dtype_code(x)
-    ws = _scratch(lib.mla_cache_append_workspace(N, d_model, d_c, d_r, code), x)
+    ws = _workspace(lib.mla_cache_append_workspace(N, d_model, d_c, d_r, code), x, workspace)
     _check("mla_cache_append", lib.mla_cache_append(
         _ptr(x), _ptr(w_c), _ptr(w_kr), _ptr(gain), float(eps), float(rope_base), _ptr(seq_ids), _ptr(positions),
         _ptr(cache), _ptr(block_table), n_seqs, stride, page_size, max_pages, num_pages, N, d_model, d_c, d_r,

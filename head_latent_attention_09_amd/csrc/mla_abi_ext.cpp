@@ -42,7 +42,7 @@ int append_splits(int n_tokens, int d_model, int d_c, int dtype) {
   GemmDesc g = gemm((const void*)16, d_model, (const void*)16, d_model, (void*)16, d_c, n_tokens, d_c, d_model,
                     dtype);
   g.out_f32 = true;
-  return gemm_nt_splits(g, kCuRef);
+  return gemm_nt_splits(g, kCuRef, 16);  // the row epilogue reads every split
 }
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -79,7 +79,7 @@ int mla_cache_append(const void* x, const void* w_c, const void* w_kr, const voi
                      size_t workspace_bytes, void* stream) {
   if (!abi_dtype_ok(dtype)) return MLA_ERR_DTYPE;
   if (n_tokens < 0 || n_seqs < 0 || d_model <= 0 || d_c <= 0 || d_r < 0 || (d_r & 1)) return MLA_ERR_SHAPE;
-  if (d_model > 65536 || d_c > 4096 || d_r > 1024) return MLA_ERR_UNSUPPORTED;
+  if (d_model > 65536 || d_c > 4096 || d_r > 1024 || d_c + d_r > 5120) return MLA_ERR_UNSUPPORTED;
   if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(rope_base) || rope_base <= 0.f) return MLA_ERR_SCALE;
   if (n_tokens == 0) return MLA_OK;
   if (!x || !w_c || (d_r > 0 && !w_kr) || !seq_ids || !positions || !latent_cache) return MLA_ERR_NULL;

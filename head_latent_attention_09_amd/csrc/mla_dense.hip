@@ -241,13 +241,18 @@ __device__ __forceinline__ void rope_angle(int pos, int i, int d, double log2_ba
 //   k_pe = rotation of z_r at positions[n]
 // written to the cache slot of (seq_ids[n], positions[n]). A token whose
 // sequence, position or page lies outside the cache is skipped (nothing is
-// written for it). One workgroup of 256 threads per token.
+// written for it). One workgroup of 256 threads per token; thread t holds
+// elements t, t + 256, ... of the row in registers (the row is at most
+// CR_EPT * 256 wide), summing the splits with independent loads.
+constexpr int CR_EPT = 20;  // d_c + d_r <= 5120
+
 template <typename T>
 __global__ __launch_bounds__(256) void cache_rows_kernel(const float* P, int splits, int64_t split_stride,
                                                          const T* gain, float eps, double log2_base,
                                                          const int32_t* seq_ids, const int32_t* positions, T* cache,
                                                          RowMap map, int n_seqs, int d_c, int d_r) {
   __shared__ float red[4];
+  __shared__ float rope_in[1024];
   const int n = blockIdx.x;
   const int W = d_c + d_r;
   const int b = seq_ids[n], pos = positions[n];
@@ -264,32 +269,46 @@ __global__ __launch_bounds__(256) void cache_rows_kernel(const float* P, int spl
   }
   T* dst = cache + slot * W;
   const float* src = P + (int64_t)n * W;
-  auto val = [&](int j) {
-    float s = 0.f;
-    for (int k = 0; k < splits; ++k) s += src[k * split_stride + j];
-    return s;
-  };
-  // latent part: sum of squares over the block, then normalise
+  float v[CR_EPT];
   float ss = 0.f;
-  for (int j = threadIdx.x; j < d_c; j += 256) {
-    const float z = val(j);
-    ss += z * z;
+#pragma unroll
+  for (int e = 0; e < CR_EPT; ++e) {
+    const int j = threadIdx.x + 256 * e;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    if (j < W) {
+      int k = 0;
+      for (; k + 4 <= splits; k += 4) {
+        a0 += src[(int64_t)k * split_stride + j];
+        a1 += src[(int64_t)(k + 1) * split_stride + j];
+        a2 += src[(int64_t)(k + 2) * split_stride + j];
+        a3 += src[(int64_t)(k + 3) * split_stride + j];
+      }
+      for (; k < splits; ++k) a0 += src[(int64_t)k * split_stride + j];
+    }
+    v[e] = (a0 + a1) + (a2 + a3);
+    if (j < d_c) ss += v[e] * v[e];
+    else if (j < W) rope_in[j - d_c] = v[e];
   }
+  // latent part: sum of squares over the block, then normalise
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float tot = red[0] + red[1] + red[2] + red[3];
   const float inv = 1.0f / sqrtf(tot / (float)d_c + eps);
-  for (int j = threadIdx.x; j < d_c; j += 256) {
-    float v = val(j) * inv;
-    if (gain) v *= load_f32(gain + j);
-    store_f32(dst + j, v);
+#pragma unroll
+  for (int e = 0; e < CR_EPT; ++e) {
+    const int j = threadIdx.x + 256 * e;
+    if (j < d_c) {
+      float x = v[e] * inv;
+      if (gain) x *= load_f32(gain + j);
+      store_f32(dst + j, x);
+    }
   }
-  // rope part, one pair per thread
+  // rope part, one pair per thread (the summed values passed through LDS)
   for (int i = threadIdx.x; i < d_r / 2; i += 256) {
     float c, s;
     rope_angle(pos, i, d_r, log2_base, c, s);
-    const float x0 = val(d_c + 2 * i), x1 = val(d_c + 2 * i + 1);
+    const float x0 = rope_in[2 * i], x1 = rope_in[2 * i + 1];
     store_f32(dst + d_c + 2 * i, x0 * c - x1 * s);
     store_f32(dst + d_c + 2 * i + 1, x0 * s + x1 * c);
   }
@@ -381,12 +400,12 @@ int launch_gemm_nt(const GemmDesc& g, hipStream_t s) {
 
 // number of split-K parts the bf16 product uses for C = A B^T of this size
 // (enough workgroups to cover the chip twice), 1 on the generic path
-int gemm_nt_splits(const GemmDesc& g, int cus) {
+int gemm_nt_splits(const GemmDesc& g, int cus, int max_splits) {
   if (!gemm_nt_mfma_ok(g)) return 1;
   const int64_t tiles = (int64_t)((g.M + dn::BM - 1) / dn::BM) * ((g.N + dn::BN - 1) / dn::BN) * g.batch;
   const int nk = g.K / dn::BK;
   int s = 1;
-  while (tiles * s < 2 * (int64_t)cus && s * 2 <= nk && s < 64) s *= 2;
+  while (tiles * s < 2 * (int64_t)cus && s * 2 <= nk && s * 2 <= max_splits) s *= 2;
   const int kps = (nk + s - 1) / s;  // slices per split; no split left empty
   return (nk + kps - 1) / kps;
 }

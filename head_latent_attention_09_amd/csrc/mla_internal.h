@@ -235,7 +235,7 @@ struct GemmDesc {
   bool out_f32;
 };
 bool gemm_nt_mfma_ok(const GemmDesc& g);
-int gemm_nt_splits(const GemmDesc& g, int cus);
+int gemm_nt_splits(const GemmDesc& g, int cus, int max_splits = 64);
 int launch_gemm_nt(const GemmDesc& g, hipStream_t s);
 int launch_splitk_reduce(const float* P, int splits, int64_t split_stride, int64_t ldp, void* C, int64_t ldc, int M,
                          int N, int dtype, hipStream_t s);

@@ -270,7 +270,7 @@ int mla_lse_combine(const float* o_parts, const float* lse_parts, int n_parts,
  * workspace: mla_cache_append_workspace(n_tokens, d_model, d_c, d_r, dtype)
  *   bytes (fp32 partial projections).
  * Status: MLA_ERR_SCALE for eps < 0, a non-finite eps or rope_base <= 0.
- * Limits: d_model <= 65536, d_c <= 4096, d_r <= 1024 and even.
+ * Limits: d_model <= 65536, d_c <= 4096, d_r <= 1024 and even, d_c + d_r <= 5120.
  * ------------------------------------------------------------------------- */
 size_t mla_cache_append_workspace(int n_tokens, int d_model, int d_c, int d_r, int dtype);
 

@@ -45,3 +45,14 @@ def lse_err(got, ref):
 
 def dtype_torch(dtype):
     return torch.bfloat16 if dtype == G.BF16 else torch.float32
+
+
+def elem_rel_err(got, ref, floor=1e-3):
+    """Largest elementwise relative error with a floor: max |g - r| / max(|r|,
+    floor * max|r|) (reported next to the infinity-norm figure; elementwise
+    relative error alone is ill-posed where the reference is near zero)."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    scale = np.max(np.abs(ref))
+    if scale == 0:
+        return float(np.max(np.abs(got)))
+    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), floor * scale)))

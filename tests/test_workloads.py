@@ -60,3 +60,10 @@ def test_rms_and_rope_properties():
     r = G.rope_interleaved(x, np.arange(7))
     np.testing.assert_allclose(np.linalg.norm(r, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12)
     np.testing.assert_array_equal(r[0], x[0])  # position 0 is the identity
+
+
+def test_paged_layout_matches_decode_case():
+    lens = [64, 1, 130, 0, 200, 65]
+    c = G.decode_case(6, 2, 8, 2, lens, G.BF16, seed=31, page_size=64)
+    table, P = G.paged_layout(lens, 64, seed=31)
+    assert np.array_equal(table, c.block_table) and P == c.pages.shape[0]

@@ -36,7 +36,7 @@ __all__ = [
     "rms_normalise", "rope_interleaved", "decode_case", "prefill_case",
     "gemm_case", "config1_notebook", "config2_decode_f32",
     "config3_decode_bf16", "config4_paged_bf16", "config5_prefill_bf16",
-    "p2_tiny_case", "xorshift32_stream", "seq_rows", "CONFIG_NAMES", "config4_lengths",
+    "p2_tiny_case", "xorshift32_stream", "seq_rows", "CONFIG_NAMES", "config4_lengths", "paged_layout",
 ]
 
 
@@ -189,6 +189,27 @@ def decode_case(B, H, d_c, d_r, lens, dtype, seed=0, *, page_size=None,
         ns.d_v = d_v
         ns.w_uv = storage(_normal(wrng, (H, d_v, d_c), 1.0 / math.sqrt(d_c)), dtype)
     return ns
+
+
+def paged_layout(lens, page_size, seed=0, shuffle_pages=True):
+    """The page layout decode_case draws for these lengths and seed, without
+    the values: (block_table [B, max_pages] int32, -1 padded; pool size P).
+    Pages are dealt in (sequence, logical page) order from a seeded
+    permutation of the pool."""
+    lens = np.asarray(lens, dtype=np.int64)
+    B = lens.shape[0]
+    npages = [(int(l) + page_size - 1) // page_size for l in lens]
+    P = int(sum(npages))
+    max_pages = max(max(npages, default=0), 1)
+    children = np.random.SeedSequence(seed).spawn(B + 2)
+    prng = np.random.default_rng(children[B + 1])
+    perm = prng.permutation(P) if shuffle_pages else np.arange(P)
+    table = np.full((B, max_pages), -1, dtype=np.int32)
+    k = 0
+    for b in range(B):
+        table[b, :npages[b]] = perm[k:k + npages[b]]
+        k += npages[b]
+    return table, P
 
 
 def seq_rows(case, b) -> np.ndarray:
