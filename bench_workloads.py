@@ -333,9 +333,50 @@ def bench_gated(M, G, torch, dev, args, time_entry):
             "roofline": dict(roof("mfma", flop, e["median"] / 1e3), alg_flop=flop)}
 
 
+# ----------------------------------------------------------------------------
+# softmax reference overflow: the decode step with and without a logit spike
+# ----------------------------------------------------------------------------
+def bench_overflow_redo(M, G, torch, dev, args, time_entry):
+    """The long-context decode step (B=64, H=128, S=4096, one call: attention
+    plus the merge fused with W_UV), first on N(0,1) inputs, then with one
+    row's scores rising by about 70 nats at position 2500 (a segment past its
+    first tile: its fixed reference overflows and the segment is redone with
+    its exact maxima)."""
+    B, H, S, d_c, d_r, d_v = 64, 128, 4096, 512, 64, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9)
+    bf = torch.bfloat16
+    cache = torch.empty((B, S, d_c + d_r), dtype=bf, device=dev)
+    for b in range(B):
+        cache[b] = _latent_rows(torch, dev, S, d_c, d_r, gen)
+    q = torch.randn((B, H, d_c + d_r), device=dev, generator=gen)
+    q[:, :, :d_c] /= math.sqrt(d_c)
+    q = q.to(bf)
+    wuv = (torch.randn((H, d_v, d_c), device=dev, generator=gen) / math.sqrt(d_c)).to(bf)
+    lens = torch.full((B,), S, dtype=torch.int32, device=dev)
+    v = torch.empty((B, H, d_v), dtype=bf, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(M.decode_up_v_workspace_bytes(B, H, d_c, M.default_workers()), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(d_c // 4 + d_r)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        M.latent_decode_up_v(q, cache, lens, d_c, scale, wuv, out=v, lse=lse, workspace=ws)
+
+    normal = time_entry(torch, stream, call, per_block=10, blocks=5)
+    q[7, :, d_c] = 40.0
+    cache[7, 2500, d_c] = 24.0  # 40 * 24 / sqrt(192) ~ 69 nats above the row's other scores
+    torch.cuda.synchronize()
+    spiked = time_entry(torch, stream, call, per_block=10, blocks=5)
+    return {"workload": "decode B=64 H=128 S=4096 (fused up-projection), normal vs one row with a ~69-nat "
+                        "logit spike at position 2500",
+            "normal_ms": normal, "spiked_ms": spiked,
+            "ratio": round(spiked["median"] / normal["median"], 3)}
+
+
 WORKLOADS = [("ragged_paged_decode", bench_ragged_paged), ("causal_prefill", bench_prefill),
              ("cache_append", bench_append), ("full_absorption", bench_full_absorption),
-             ("gated_mla", bench_gated)]
+             ("gated_mla", bench_gated), ("overflow_redo", bench_overflow_redo)]
 
 
 def run_all(M, G, torch, dev, args, time_entry):

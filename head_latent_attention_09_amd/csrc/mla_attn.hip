@@ -388,7 +388,8 @@ constexpr float SLACK = 0x1p64f;             // bound on a segment's sum of weig
 constexpr int LDS_QR = NBUF * TILE_BYTES;
 constexpr int LDS_P = LDS_QR + NW * QR_BYTES;
 constexpr int LDS_INV = LDS_P + 2 * P_BYTES;
-constexpr int SMEM_BYTES = LDS_INV + 32 * NW * 4;
+constexpr int LDS_MFIX = LDS_INV + 32 * NW * 4;   // a redo's softmax reference per head
+constexpr int SMEM_BYTES = LDS_MFIX + 32 * NW * 4;
 
 // Work split inside a workgroup (4 waves, one per SIMD). Scores and softmax
 // weights are split by head: wave w owns heads 32w .. 32w+31 and computes
@@ -594,9 +595,11 @@ __device__ __forceinline__ void issue_tile(const TileSrc& s, char* buf, int lx, 
 }
 
 
-// Whole-row recompute with the generic kernel (running max with rescaling),
-// writing the final result; the tile ring is reused as its scratch.
-__device__ void recompute_row(const Args& a, int r, int len, char* smem) {
+// A segment redone by the generic kernel's code (running maximum with
+// rescaling, 8 heads at a time), writing the same outputs as attend_segment:
+// for a segment whose weights overflowed fp32 (a score 128 or more log2
+// units above its first tile's maximum). The tile ring serves as its scratch.
+__device__ void generic_segment(const Args& a, int r, int len, int lt0, int lt1, bool full, int slot, char* smem) {
   gn::Args<bf16> ga;
   ga.q = a.q;
   ga.cache = a.cache;
@@ -613,15 +616,24 @@ __device__ void recompute_row(const Args& a, int r, int len, char* smem) {
   float* ps = qs + gn::HG * gn::WMAX;
   float* alpha_s = ps + gn::HG * gn::TT;
   float* stat_s = alpha_s + gn::HG;
+  static_assert((gn::TT * (gn::WMAX + 1) + gn::HG * (gn::WMAX + gn::TT + 3)) * 4 <= SMEM_BYTES, "generic scratch");
   float m_run = -INFINITY, l_run = 0.f;
   for (int h0 = 0; h0 < a.H; h0 += gn::HG)
-    gn::attend_segment<bf16>(ga, r, len, 0, (len + gn::TT - 1) / gn::TT, true, 0, h0, tile, qs, ps, alpha_s,
-                             stat_s, m_run, l_run);
+    gn::attend_segment<bf16>(ga, r, len, lt0, lt1, full, slot, h0, tile, qs, ps, alpha_s, stat_s, m_run, l_run);
   __syncthreads();
 }
 
+// One segment (tiles lt0 .. lt1-1 of row r). On a first pass the softmax
+// reference of each owned head is the largest score of the first tile; on a
+// redo (seg_flag[1] set) it is the reference stored at LDS_MFIX. Returns 0
+// once the segment's outputs are written. When the first-tile reference
+// overflowed (see the reference note at the end) it writes nothing and
+// returns 1, having stored a safe reference for a redo and set seg_flag[1],
+// or 2 when the weights themselves overflowed. The redo state lives in LDS,
+// not registers: values held in registers across the segment pushed the
+// kernel into spills whose reloads drain the tile loads in flight.
 template <int NHB, bool STREAM>
-__device__ __forceinline__ void attend_segment(const Args& a, int r, int len, int lt0, int lt1, bool full, int slot,
+__device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int lt0, int lt1, bool full, int slot,
                                                char* smem, int* seg_flag, int lane, int wv) {
   constexpr int H = 32 * NHB;
   const int b = row_batch(a.map, r);
@@ -634,6 +646,7 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int len, in
   const int L = loads_per_tile(wv);
   char* const qr_lds = smem + LDS_QR + wv * QR_BYTES;
   float* const inv_s = (float*)(smem + LDS_INV);
+  float* const m_fix_s = (float*)(smem + LDS_MFIX);
   auto tbuf = [&](int j) { return smem + (j % NBUF) * TILE_BYTES; };
 
   // every wave must be done with the previous segment's LDS (and flag)
@@ -796,6 +809,10 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int len, in
       mx = fmaxf(mx, shfl_xor(mx, ln, 32));
       m_ref[hb] = mx;
     }
+    if (seg_flag[1]) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) m_ref[hb] = m_fix_s[wv * 32 + hb * 16 + t16] * kLog2e + 1.f;
+    }
   }
   if (owner && ntiles > 1) kprefetch(TILE_BYTES);
 
@@ -911,39 +928,48 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int len, in
   // of the segment's first tile and the weights are 2^(x - m_ref). Keeping
   // the reference fixed keeps the output accumulator free of data-dependent
   // rescaling (a conditional rescale moves it out of the accumulation
-  // registers). A later score far above m_ref shows in the sum of weights:
-  // a segment whose sum reaches SLACK = 2^64 (or is inf or NaN) flags its
-  // row, and the first workgroup to flag row r recomputes the whole row with
-  // the generic running-max kernel into the final output; the combine skips
-  // flagged rows. Any score more than 64 (log2 units) above m_ref gives such
-  // a sum; below it the weights, sums and outputs stay far inside the range
-  // of bf16 and fp32.
+  // registers). A later score far above m_ref shows in the sum of weights l:
+  // a segment whose sum reaches SLACK = 2^64 is abandoned before anything is
+  // written and redone alone. While l is finite it bounds every weight, so
+  // the largest score x_max (log2 units) of each head satisfies
+  // x_max <= m_ref + log2 l + 2^-8 (bf16 rounding of a weight) and
+  // x_max >= m_ref + log2 l - log2 n (n positions): the redo takes
+  // m_ref + log2 l + 1 as the reference, its weights are at most 1/2 and the
+  // largest at least 1/(4n), so it neither overflows nor underflows. A sum
+  // that is inf or NaN (a weight past the fp32 range: a score 128 or more
+  // above m_ref) sends the segment to the generic running-max code. Either
+  // way only this segment is redone; the combine merges it like any other
+  // part. Measured on the B=64, S=4096 decode: a 69-nat spike in one row
+  // costs 1.4x the normal call; the redo path makes the normal call about
+  // 1 % slower than a kernel without one, where a running maximum kept in
+  // the tile loop cost 3 %. Below 64 (log2 units) above m_ref the weights,
+  // sums and outputs stay far inside the range of bf16 and fp32.
   int le = lane;  // per-lane values of the epilogue stay here (see the tile loop)
   opaque(le);
   float lse_v[2] = {0.f, 0.f};
   if (owner) {
-    bool over = false;
+    bool over = false, inf = false;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       float l = lsum[hb];
       l += shfl_xor(l, le, 16);
       l += shfl_xor(l, le, 32);
       over |= !(l < SLACK);  // also catches inf and NaN
+      inf |= !(l < INFINITY);
       lse_v[hb] = (m_ref[hb] + __log2f(l)) * kLn2;
-      if (le < 16) inv_s[wv * 32 + hb * 16 + le] = 1.0f / l;
+      if (le < 16) {
+        inv_s[wv * 32 + hb * 16 + le] = 1.0f / l;
+        m_fix_s[wv * 32 + hb * 16 + le] = lse_v[hb];  // a redo's reference is m_ref + log2 l + 1
+      }
     }
-    if (__any(over) && le == 0) atomicOr(seg_flag, 1);
+    const bool any_inf = __any(inf);
+    if (__any(over) && le == 0) atomicOr(seg_flag, any_inf ? 3 : 1);
   }
   __syncthreads();
   if (*seg_flag) {
-    // Recompute the whole row into the final output; a part of a split row
-    // also marks its lse slots (NaN) so that the combine leaves the row as
-    // it is. Every flagged part of a row recomputes it: the writes are the
-    // same values.
-    if (!full)
-      for (int h = threadIdx.x; h < H; h += blockDim.x) a.pl.part_lse[(size_t)slot * H + h] = __builtin_nanf("");
-    recompute_row(a, r, len, smem);
-    return;
+    const int st = (*seg_flag & 2) ? 2 : 1;
+    if (st == 1 && threadIdx.x == 0) seg_flag[1] = 1;  // read by every thread before the barrier above
+    return st;
   }
 
   // ---- finish: normalise, write the final row or this worker's partial (bf16)
@@ -993,6 +1019,7 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int len, in
       *(bf16x8*)(dst + (size_t)(64 * half + i) * DC + 8 * le) = *(const MLA_LDS bf16x8*)(smem + i * OROW + 16 * le);
     __syncthreads();  // the staging rows are read before the next half overwrites them
   }
+  return 0;
 }
 
 // SELF: the workgroup plans for itself (self_plan) instead of reading the
@@ -1000,12 +1027,13 @@ __device__ __forceinline__ void attend_segment(const Args& a, int r, int len, in
 template <int NHB, bool STREAM, bool SELF>
 __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(Args a) {
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
-  __shared__ int seg_flag;
+  __shared__ int seg_flag[2];  // [0] overflow of this pass, [1] the pass is a redo
   __shared__ int cum_s[SELF ? SELF_MAX_R + 1 : 1], len_s[SELF ? SELF_MAX_R : 1];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int G = a.pl.G, R = a.pl.R;
   const int w = xcd_worker(blockIdx.x, G);
+  if (threadIdx.x == 0) seg_flag[1] = 0;  // published by the first segment's opening barrier
   int total, seg_cost;
   if constexpr (SELF) {
     self_plan(a.map, R, G, TILE, cum_s, len_s, seg_cost, total);
@@ -1043,7 +1071,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(Args a) {
     Segment sg;
     if (!plan_segment(c0, c1, seg_cost, t_begin, t_end, w, per, sg)) continue;
     const int len = SELF ? __builtin_amdgcn_readfirstlane(len_s[r]) : a.pl.len[r];
-    attend_segment<NHB, STREAM>(a, r, len, sg.lt0, sg.lt1, sg.full, sg.slot, smem, &seg_flag, lane, wv);
+    // a redo with the bound from the sum of weights, or the generic code
+    // (also for a second overflow, possible only for non-finite inputs); two
+    // call sites measured faster than one inside a loop
+    int st = attend_segment<NHB, STREAM>(a, r, len, sg.lt0, sg.lt1, sg.full, sg.slot, smem, seg_flag, lane, wv);
+    if (st == 1)
+      st = attend_segment<NHB, STREAM>(a, r, len, sg.lt0, sg.lt1, sg.full, sg.slot, smem, seg_flag, lane, wv);
+    if (st != 0) generic_segment(a, r, len, sg.lt0, sg.lt1, sg.full, sg.slot, smem);
+    if (threadIdx.x == 0) seg_flag[1] = 0;  // its last reads precede the segment's final barrier
   }
 }
 }  // namespace mf
@@ -1091,8 +1126,7 @@ __device__ void combine_head(int n, PartFn part, int d_c, OutT* out, float* lse_
 // 0 in slot s0, part i > 0 in slot 2(w0 + i) (the row started before those
 // workers' ranges). Each thread issues the lse and partial loads of up to NP
 // parts at once, then merges them with a running maximum, so a workgroup
-// waits for memory twice (list entry, then data). A row with a part whose
-// lse is NaN was recomputed by the attention kernel and is already final.
+// waits for memory twice (list entry, then data).
 // Merge of the n parts of split row r for one item (VEC dims d.. of head h):
 // part 0 in slot s0, part i > 0 in slot 2(w0 + i).
 template <typename OutT, int VEC>
@@ -1100,7 +1134,6 @@ __device__ __forceinline__ void merge_item(const Plan& pl, int H, int d_c, int r
                                            int d, OutT* out, float* lse) {
   constexpr int NP = 4;
   typedef OutT vec_t __attribute__((ext_vector_type(VEC)));
-  bool marked = false;  // a part recomputed the row
   float mx = -INFINITY, ws = 0.f;
   float acc[VEC];
 #pragma unroll
@@ -1114,7 +1147,6 @@ __device__ __forceinline__ void merge_item(const Plan& pl, int H, int d_c, int r
       const int slot = i == 0 ? s0 : 2 * (w0 + i);
       l[j] = p0 + j < n ? pl.part_lse[(size_t)slot * H + h] : -INFINITY;
       v[j] = *(const vec_t*)((const OutT*)pl.part_o + ((size_t)slot * H + h) * d_c + d);
-      marked |= l[j] != l[j];
     }
     float m2 = mx;
 #pragma unroll
@@ -1133,7 +1165,6 @@ __device__ __forceinline__ void merge_item(const Plan& pl, int H, int d_c, int r
     }
     mx = m2;
   }
-  if (marked) return;
   const float inv = ws > 0.f ? 1.0f / ws : 0.f;
   vec_t o;
 #pragma unroll

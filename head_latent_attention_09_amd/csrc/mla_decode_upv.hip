@@ -12,7 +12,7 @@ namespace mla {
 
 // Workgroup (row block, head): A = the 32 rows' latent outputs of head h,
 // built in LDS from the attention kernel's results -- a row one worker
-// finished (or recomputed) is read from `lat`, a cut row is merged from its
+// finished is read from `lat`, a cut row is merged from its
 // partial outputs (the combine's merge), an empty row is zero -- then
 // v[rows, h, :] = A W_UV[h]^T with 32x32x16 bf16 MFMA. Saves the combine
 // kernel and the round trip of the merged rows through HBM.
@@ -59,7 +59,6 @@ __global__ __launch_bounds__(512, 1) void upv_merge_kernel(Plan pl, int H, const
     const int row = tid >> 3, k = tid & 7, r = n0 + row;
     int kind = 0, s0 = 0, w0 = 0, np = 0;
     float mx = -INFINITY, ws = 0.f, l_first = -INFINITY;
-    bool marked = false;
     // every plan entry in one round of loads (rows past the batch read the last row's)
     const int rc = r < R ? r : R - 1;
     const int len = pl.len[rc], base = pl.cum[rc], n = pl.cum[rc + 1] - base, total = pl.cum[R], c = pl.split[1];
@@ -76,7 +75,6 @@ __global__ __launch_bounds__(512, 1) void upv_merge_kernel(Plan pl, int H, const
         for (int i = k; i < np; i += FPW) {
           const float l = pl.part_lse[(size_t)(i == 0 ? s0 : 2 * (w0 + i)) * H + h];
           if (i == k) l_first = l;
-          marked |= l != l;
           if (l > mx) {
             ws = ws * __expf(mx - l) + 1.f;
             mx = l;
@@ -89,13 +87,12 @@ __global__ __launch_bounds__(512, 1) void upv_merge_kernel(Plan pl, int H, const
 #pragma unroll
     for (int off = 1; off < FPW; off <<= 1) {
       const float om = __shfl_xor(mx, off), ow = __shfl_xor(ws, off);
-      marked |= __shfl_xor((int)marked, off) != 0;
       const float m2 = fmaxf(mx, om);
       ws = (mx == -INFINITY ? 0.f : ws * __expf(mx - m2)) + (om == -INFINITY ? 0.f : ow * __expf(om - m2));
       mx = m2;
     }
     float l_tot = -INFINITY;
-    if (kind == 1 && np > 0 && !marked) {  // a marked row was recomputed into `lat`
+    if (kind == 1 && np > 0) {
       kind = 2;
       l_tot = ws > 0.f ? mx + __logf(ws) : -INFINITY;
     }

@@ -166,7 +166,7 @@ def test_decode_up_v_events_and_no_lse():
 
 @pytest.mark.parametrize("workers", [4, 1])
 def test_decode_up_v_large_logits(workers):
-    """The recompute path of overflowing rows under the fused merge."""
+    """Segments redone after a softmax reference overflow, under the fused merge."""
     case = G.decode_case(2, 128, 512, 64, [600, 300], G.BF16, seed=13, d_v=128)
     case.kq_scale = 1.0 / math.sqrt(192)
     cache = G.to_f64(case.cache, G.BF16)
@@ -300,9 +300,10 @@ def test_decode_zero_query_is_mean():
 
 @pytest.mark.parametrize("workers", [4, 1])
 def test_decode_large_logits_fixup(workers):
-    """Scores that rise by far more than 2^32 within a sequence (handled by the
-    recompute path of rows whose fixed softmax reference overflowed): rows cut
-    over several workers (4) and rows finished by one worker (1)."""
+    """Scores that rise steadily by far more than 2^64 along a sequence
+    (segments whose first-tile softmax reference overflows are redone with
+    their exact maxima): rows cut over several workers (4) and rows finished
+    by one worker (1)."""
     case = G.decode_case(2, 128, 512, 64, [600, 300], G.BF16, seed=13)
     case.kq_scale = 1.0 / math.sqrt(192)
     cache = G.to_f64(case.cache, G.BF16)
@@ -313,6 +314,39 @@ def test_decode_large_logits_fixup(workers):
     q[:, :, 512] = 40.0
     case.q = G.storage(q, G.BF16)
     check_decode(case, num_workers=workers, label="large logits")
+
+
+def _spike(case, b, pos, value, coord=512):
+    """Set rope coordinate `coord` of cache row (b, pos) to `value` (dense or paged)."""
+    if case.page_size is None:
+        x = G.to_f64(case.cache[b, pos], case.dtype)
+        x[coord] = value
+        case.cache[b, pos] = G.storage(x, case.dtype)
+    else:
+        pg = int(case.block_table[b, pos // case.page_size])
+        x = G.to_f64(case.pages[pg, pos % case.page_size], case.dtype)
+        x[coord] = value
+        case.pages[pg, pos % case.page_size] = G.storage(x, case.dtype)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("workers", [16, 1])
+def test_decode_overflow_redo_later_segment(workers, paged):
+    """Isolated logit spikes in the middle of long rows, against the oracle on
+    every head: row 0 rises by about 60 nats over the rest (sum of weights
+    past 2^64 but finite), row 1 by about 150 nats (weights overflow to inf),
+    row 2 has its spike in the first tile (no redo), row 3 none. With 16
+    workers the rows are cut across workers, so the redone segments are parts
+    of split rows; with 1 worker each row is one segment."""
+    case = G.decode_case(4, 128, 512, 64, [2000, 1500, 1000, 700], G.BF16, seed=21,
+                         page_size=64 if paged else None)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    q = G.to_f64(case.q, G.BF16)
+    q[:, :, 512] = 40.0
+    case.q = G.storage(q, G.BF16)
+    for b, pos, val in [(0, 1517, 24.0), (0, 1701, 24.0), (1, 1211, 52.0), (2, 5, 24.0)]:
+        _spike(case, b, pos, val)
+    check_decode(case, num_workers=workers, label="overflow redo")
 
 
 # ----------------------------------------------------------------------------
