@@ -22,10 +22,13 @@ bounded sample of the same workload on this host.
 `workloads` holds the other measured workloads, each with its own roofline:
 the ragged paged decode (B=128, lengths U[1, 32768], 64-position pages), the
 causal prefill B=2 S=4096 H=128 in both forms (absorbed chain and expanded
-per-head form), the fused cache append, full absorption, and the gated MLA
-layer (--headline-only skips them).
+per-head form), the fused cache append, full absorption, the gated MLA
+layer, and the decode step with a logit spike that makes one segment redo
+its softmax (--headline-only skips them; --skip-headline runs only them,
+--only picks some).
 
-    python bench.py [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--headline-only | --skip-headline] [--only a,b]
+                    [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -67,6 +70,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     p.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     p.add_argument("--only", default="", help="comma-separated subset of the other workloads")
+    p.add_argument("--skip-headline", action="store_true",
+                   help="run only the other workloads (for profiling them without the headline's kernels)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
@@ -138,6 +143,13 @@ def main():
 
     assert torch.cuda.is_available(), "no HIP device"
     dev = torch.device("cuda:0")
+    if args.skip_headline:
+        import bench_workloads as BW
+        line = {"headline": "skipped", "workloads": BW.run_all(M, G, torch, dev, args, time_entry)}
+        if args.copy_calibration:
+            copy_calibration(torch, dev)
+        print(json.dumps(line), flush=True)
+        return
     case = G.config3_decode_bf16(0)
 
     def to_dev(a):
@@ -212,11 +224,7 @@ def main():
     attn_avg = float(np.mean(attn_ms))
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+        copy_calibration(torch, dev)
 
     tokens = B * H * S
     value = tokens / (ms_step / 1e3)
@@ -260,6 +268,16 @@ def main():
         import bench_workloads as BW
         line["workloads"] = BW.run_all(M, G, torch, dev, args, time_entry)
     print(json.dumps(line), flush=True)
+
+
+def copy_calibration(torch, dev):
+    """Three plain 1 GiB device copies: their HBM counter readings scale the
+    attention kernel's."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def time_entry(torch, stream, call, per_block=20, blocks=5):
