@@ -209,40 +209,66 @@ __global__ __launch_bounds__(NT, 2) void flash_kernel(Args a) {
           s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mb], 0, 0, 0);
         }
       }
-      // ---- online softmax. Lane holds key 32 mb + 8 (r / 4) + 4 g + r % 4 of its query.
+      // ---- online softmax. Lane holds key 32 mb + 8 (r / 4) + 4 g + r % 4 of
+      // its query. A full block (every key visible) with a positive scale
+      // takes the maximum of the raw scores and folds the scale into one
+      // fused multiply-add per weight; diagonal and tail blocks scale, mask
+      // and take the maximum of the scaled scores (then sc = 1).
       const bool full = k0 + KB <= a.S_kv && (!CAUSAL || k0 + KB - 1 <= qw0 + off);
-      float mx = -INFINITY;
+      const bool fast = full && a.scale_log2 > 0.f;  // wave-uniform
+      float mx;
+      float sc = a.scale_log2;
+      if (fast) {
+        float m0 = fmaxf(s[0][0], s[0][1]), m1 = fmaxf(s[1][0], s[1][1]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int r = 2; r < 16; r += 2) {
+          m0 = fmaxf(m0, fmaxf(s[0][r], s[0][r + 1]));
+          m1 = fmaxf(m1, fmaxf(s[1][r], s[1][r + 1]));
+        }
+        mx = fmaxf(m0, m1) * sc;
+      } else {
+        mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[mb][r] * a.scale_log2;
-          if (!full) {
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
             const int kk = k0 + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
             const bool ok = kk < a.S_kv && (!CAUSAL || kk <= qi + off);
-            x = ok ? x : -INFINITY;
+            const float x = ok ? s[mb][r] * sc : -INFINITY;
+            s[mb][r] = x;
+            mx = fmaxf(mx, x);
           }
-          s[mb][r] = x;
-          mx = fmaxf(mx, x);
-        }
+        sc = 1.f;
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // The reference moves only when the maximum rises by more than 8 (log2
+      // units): weights stay below 2^8, and the output is rescaled (64
+      // multiplies per lane) only in the blocks where a reference moves.
       const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
+      const bool bump = m_new > m_run + 8.f;  // also true for the first visible block
+      const float m_next = bump ? m_new : m_run;
+      const float m_use = m_next == -INFINITY ? 0.f : m_next;
+      const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
+      m_run = m_next;
       bf16x8 pf[4];  // B operand of the value MFMA for key k-steps 0..3
       float psum = 0.f;
+      const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           bf16x8 p8;
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const float w = __builtin_amdgcn_exp2f(s[mb][8 * jj + t] - m_use);
-            const bf16 wb = f32_to_bf16(w);
-            p8[t] = wb;
-            psum += (float)wb;  // the denominator sums exactly the rounded weights the MFMA uses
+          for (int t = 0; t < 8; t += 2) {
+            const float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][8 * jj + t], sc, -m_use));
+            const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][8 * jj + t + 1], sc, -m_use));
+            bf16x2 q2;
+            q2[0] = f32_to_bf16(w0);
+            q2[1] = f32_to_bf16(w1);
+            p8[t] = q2[0];
+            p8[t + 1] = q2[1];
+            // the denominator sums exactly the rounded weights the MFMA uses
+            psum = __builtin_amdgcn_fdot2_f32_bf16(q2, ones, psum, false);
           }
           pf[2 * mb + jj] = p8;
         }
