@@ -177,17 +177,11 @@ int mla_prefill_unabsorbed(const void* q_nope, const void* q_pe, const void* lat
   const int W = d_c + d_r, KV = d_nope + d_v;
   bf16* kv = (bf16*)workspace;  // [batch * s_kv, n_heads, d_nope + d_v]: k_nope | v per head
   if (s_kv > 0) {
-    // k_nope[t, h] = W_UK[h] c_t and v[t, h] = W_UV[h] c_t (c_t: the first d_c values of cache row t)
-    GemmDesc gk = gemm(latent_cache, W, w_uk, d_c, kv, (int64_t)n_heads * KV, batch * s_kv, d_nope, d_c, dtype);
-    gk.batch = n_heads;
-    gk.b_batch = (int64_t)d_nope * d_c;
-    gk.c_batch = KV;
-    MLA_TRY(launch_gemm_nt(gk, s));
-    GemmDesc gv = gemm(latent_cache, W, w_uv, d_c, kv + d_nope, (int64_t)n_heads * KV, batch * s_kv, d_v, d_c, dtype);
-    gv.batch = n_heads;
-    gv.b_batch = (int64_t)d_v * d_c;
-    gv.c_batch = KV;
-    MLA_TRY(launch_gemm_nt(gv, s));
+    // k_nope[t, h] = W_UK[h] c_t and v[t, h] = W_UV[h] c_t (c_t: the first d_c values of cache row t),
+    // as one product: output row t = [k_nope | v] of every head, B rows alternating d_nope rows of
+    // W_UK[h] and d_v rows of W_UV[h]
+    MLA_TRY(launch_gemm_pair(latent_cache, W, w_uk, w_uv, d_c, d_nope, d_v, kv, (int64_t)n_heads * KV,
+                             batch * s_kv, n_heads * KV, d_c, s));
   }
   FlashDesc f{};
   f.q = q_nope;

@@ -344,6 +344,161 @@ __global__ __launch_bounds__(256) void gate_kernel(T* x, const T* gt, int64_t n)
   const float gv = load_f32(gt + i);
   store_f32(x + i, load_f32(x + i) * (1.0f / (1.0f + __expf(-gv))));
 }
+
+// ---------------------------------------------------------------------------
+// Large product with B rows gathered from two matrices: C[m, n] = sum_k
+// A[m, k] B(n)[k] (bf16 in and out), where row n of B belongs to group
+// g = n / (n1 + n2): its first n1 rows are rows g n1 .. of B1, the next n2
+// rows g n2 .. of B2. The per-head key and value expansions of the latent
+// rows (k[t,h] = W_UK[h] c_t, v[t,h] = W_UV[h] c_t) run as ONE product whose
+// output row holds [k_nope | v] for every head, instead of one product per
+// head and tensor that re-reads the latent rows each time.
+// 256 x 256 outputs per workgroup of 8 waves (2 x 4, each 128 x 64), 64-wide
+// K slices of A and B in LDS (two stages of 64 KiB, direct loads). The MFMA
+// takes the B rows as its first operand, so each lane's accumulator holds 4
+// consecutive output columns of one row: the bf16 output goes to the LDS
+// staging area as 8-byte runs and to HBM as whole 16-byte chunks.
+// ---------------------------------------------------------------------------
+constexpr int PM = 256, PN = 256, PNT = 512;
+constexpr int PA_BYTES = PM * BK * 2;        // 32 KiB
+constexpr int PB_BYTES = PN * BK * 2;        // 32 KiB
+constexpr int PSTAGE = PA_BYTES + PB_BYTES;  // 64 KiB
+
+struct PairArgs {
+  const bf16* A;
+  int64_t lda;
+  const bf16* B1;
+  const bf16* B2;
+  int64_t ldb;
+  int n1, n2;
+  bf16* C;
+  int64_t ldc;
+  int M, N, K;
+  int band, ntn;  // M tiles per XCD, N tiles
+};
+
+// Workgroups are dealt to the 8 XCDs round-robin by index; workgroup i runs
+// on XCD i % 8. Each XCD takes a band of M tiles (its A rows stay in that
+// XCD's L2) and walks every N tile, so A is read from memory about once and
+// each B tile once per XCD.
+__global__ __launch_bounds__(PNT, 1) void gemm_pair_kernel(PairArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * PSTAGE];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = lane >> 5;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int mt = xcd * a.band + local % a.band, nt = local / a.band;
+  if (mt * PM >= a.M || nt >= a.ntn) return;  // past the last tile (whole workgroup)
+  const int m0 = mt * PM, n0 = nt * PN;
+  const int wm = wv >> 2, wn = wv & 3;
+  const int nk = a.K / BK;
+
+  // the rows this lane loads (fixed over the K slices): loads i = 0..3 of A
+  // and of B, 64 lanes x 16 bytes each, cover rows (4 wv + i) * 8 + lane / 8
+  const bf16* arow[4];
+  const bf16* brow[4];
+  int coff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = (wv * 4 + i) * 64 + lane;
+    const int row = p >> 3;
+    coff[i] = ((p & 7) ^ swz8(row)) * 8;
+    int m = m0 + row;
+    m = m < a.M ? m : a.M - 1;
+    arow[i] = a.A + (int64_t)m * a.lda;
+    int n = n0 + row;
+    n = n < a.N ? n : a.N - 1;
+    const int gs = a.n1 + a.n2;
+    const int grp = n / gs, j = n - grp * gs;
+    brow[i] = j < a.n1 ? a.B1 + ((int64_t)grp * a.n1 + j) * a.ldb
+                       : a.B2 + ((int64_t)grp * a.n2 + (j - a.n1)) * a.ldb;
+  }
+  auto issue = [&](int kc, char* st) {
+    const int k0 = kc * BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(arow[i] + k0 + coff[i]),
+                                       (MLA_LDS void*)(st + (wv * 4 + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(brow[i] + k0 + coff[i]),
+                                       (MLA_LDS void*)(st + PA_BYTES + (wv * 4 + i) * 1024), 16, 0, 0);
+  };
+
+  f32x16 acc[4][2];  // [m block][n block], C^T layout: lane l = row m, registers = 4 consecutive n
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  if (nk > 0) issue(0, smem);
+  if (nk > 1) issue(1, smem + PSTAGE);
+  for (int kc = 0; kc < nk; ++kc) {
+    // this wave's 8 loads of slice kc have landed (the next slice's 8 may be in flight) ...
+    if (kc + 1 < nk) __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));
+    else __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    barrier();  // ... and every other wave's
+    const char* sa = smem + (kc & 1) * PSTAGE;
+    const char* sb = sa + PA_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + i * 32 + (lane & 31);
+        af[i] = *(const MLA_LDS bf16x8*)(sa + row * 128 + (((2 * ks + g) ^ swz8(row)) * 16));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = wn * 64 + j * 32 + (lane & 31);
+        bfr[j] = *(const MLA_LDS bf16x8*)(sb + row * 128 + (((2 * ks + g) ^ swz8(row)) * 16));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    }
+    if (kc + 2 < nk) {
+      barrier();  // every wave is done with this buffer
+      issue(kc + 2, smem + (kc & 1) * PSTAGE);
+    }
+  }
+
+  // output, 128 rows at a time through LDS (rows of 256 bf16 + 16 bytes of padding)
+  constexpr int OROW = PN * 2 + 16;
+  static_assert(128 * OROW <= 2 * PSTAGE, "half the output tile fits the stage buffers");
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    barrier();  // the stage buffers (or the previous half) are free
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int row = i * 32 + (lane & 31);  // within the half
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = wn * 64 + j * 32 + 8 * q + 4 * g;
+            bf16x4 v;
+            v[0] = f32_to_bf16(acc[i][j][4 * q + 0]);
+            v[1] = f32_to_bf16(acc[i][j][4 * q + 1]);
+            v[2] = f32_to_bf16(acc[i][j][4 * q + 2]);
+            v[3] = f32_to_bf16(acc[i][j][4 * q + 3]);
+            *(MLA_LDS bf16x4*)(smem + row * OROW + col * 2) = v;
+          }
+        }
+    }
+    barrier();
+#pragma unroll
+    for (int it = 0; it < 128 * (PN / 8) / PNT; ++it) {
+      const int idx = it * PNT + threadIdx.x;
+      const int row = idx >> 5, ch = idx & 31;
+      const int m = m0 + half * 128 + row, n = n0 + ch * 8;
+      if (m < a.M && n < a.N)
+        *(bf16x8*)(a.C + (int64_t)m * a.ldc + n) = *(const MLA_LDS bf16x8*)(smem + row * OROW + ch * 16);
+    }
+  }
+}
 }  // namespace dn
 
 // ===========================================================================
@@ -355,6 +510,22 @@ bool gemm_nt_mfma_ok(const GemmDesc& g) {
   return g.dtype == MLA_BF16 && g.K % dn::BK == 0 && g.K > 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
          g.a_batch % 8 == 0 && g.b_batch % 8 == 0 && al16(g.A) && al16(g.B) &&
          (g.out_f32 || (g.N % 8 == 0 && g.ldc % 8 == 0 && g.c_batch % 8 == 0 && al16(g.C)));
+}
+
+int launch_gemm_pair(const void* A, int64_t lda, const void* B1, const void* B2, int64_t ldb, int n1, int n2,
+                     void* C, int64_t ldc, int M, int N, int K, hipStream_t s) {
+  if (M <= 0 || N <= 0) return MLA_OK;
+  if (K % dn::BK != 0 || K <= 0 || lda % 8 || ldb % 8 || ldc % 8 || N % 8 || n1 <= 0 || n2 < 0 || !al16(A) ||
+      !al16(B1) || (n2 > 0 && !al16(B2)) || !al16(C))
+    return MLA_ERR_UNSUPPORTED;
+  const int mtiles = (M + dn::PM - 1) / dn::PM, ntiles = (N + dn::PN - 1) / dn::PN;
+  const int band = (mtiles + 7) / 8;
+  if ((int64_t)8 * band * ntiles > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  dn::PairArgs a{(const bf16*)A, lda, (const bf16*)B1, (const bf16*)B2, ldb, n1, n2, (bf16*)C, ldc, M, N, K,
+                 band, ntiles};
+  dim3 grid((unsigned)(8 * band * ntiles));
+  hipLaunchKernelGGL(dn::gemm_pair_kernel, grid, dim3(dn::PNT), 0, s, a);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 int launch_gemm_nt(const GemmDesc& g, hipStream_t s) {

@@ -237,6 +237,11 @@ struct GemmDesc {
 bool gemm_nt_mfma_ok(const GemmDesc& g);
 int gemm_nt_splits(const GemmDesc& g, int cus, int max_splits = 64);
 int launch_gemm_nt(const GemmDesc& g, hipStream_t s);
+// bf16 C[m, n] = sum_k A[m, k] B(n)[k] for large M and N, row n of B taken
+// from B1 or B2 in groups of n1 + n2 rows (see mla_dense.hip); K a multiple
+// of 64, N a multiple of 8, 16-byte aligned rows
+int launch_gemm_pair(const void* A, int64_t lda, const void* B1, const void* B2, int64_t ldb, int n1, int n2,
+                     void* C, int64_t ldc, int M, int N, int K, hipStream_t s);
 int launch_splitk_reduce(const float* P, int splits, int64_t split_stride, int64_t ldp, void* C, int64_t ldc, int M,
                          int N, int dtype, hipStream_t s);
 int launch_transpose(const void* in, void* out, int rows, int cols, int batch, int64_t in_batch, int64_t out_batch,
