@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["mla_abi.cpp", "mla_abi_ext.cpp", "mla_attn.hip", "mla_decode_upv.hip", "mla_gemm.hip", "mla_dense.hip", "mla_flash.hip"]
+SOURCES = ["mla_abi.cpp", "mla_abi_ext.cpp", "mla_attn.hip", "mla_decode_upv.hip", "mla_gemm.hip", "mla_dense.hip", "mla_flash.hip", "mla_stream.hip"]
 ARCH = "gfx950"
 
 

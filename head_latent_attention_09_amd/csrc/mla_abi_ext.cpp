@@ -47,12 +47,36 @@ int append_splits(int n_tokens, int d_model, int d_c, int dtype) {
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// out_absorbed: split count of out[N, d_model] = lat[N, H d_c] a_vo^T
+// out_absorbed: split count of out[N, d_model] = lat[N, H d_c] a_vo^T on the
+// tiled product
 int out_splits(int64_t n_tokens, int n_heads, int d_c, int d_model, int dtype) {
   GemmDesc g = gemm((const void*)16, (int64_t)n_heads * d_c, (const void*)16, (int64_t)n_heads * d_c, (void*)16,
                     d_model, (int)n_tokens, d_model, n_heads * d_c, dtype);
   g.out_f32 = true;
   return gemm_nt_splits(g, kCuRef);
+}
+
+// out_absorbed on the weight stream (at most 64 tokens): the same product with
+// split-K partials; its split count never exceeds the tiled product's, so one
+// workspace size serves both
+StreamDesc out_stream(const void* out_lat, const void* a_vo, float* P, int64_t n_tokens, int n_heads, int d_c,
+                      int d_model, int dtype) {
+  StreamDesc d{};
+  const int K = n_heads * d_c;
+  d.X = out_lat;
+  d.ldx = K;
+  d.W = a_vo;
+  d.ldw = K;
+  d.P = P;
+  d.p_split = n_tokens * d_model;
+  d.M = (int)n_tokens;
+  d.N = d_model;
+  d.K = K;
+  d.splits = 0;
+  if (dtype != MLA_BF16 || n_tokens > 64) return d;
+  const int cap = out_splits(n_tokens, n_heads, d_c, d_model, dtype);
+  d.splits = stream_gemm_splits(d_model, K, kCuRef, cap);
+  return d;
 }
 
 bool gated_flash_route(int d_model, int n_heads, int dtype) {
@@ -308,8 +332,13 @@ int mla_out_absorbed(const void* out_lat, const void* a_vo, void* out, int64_t n
   if (workspace_bytes < mla_out_absorbed_workspace(n_tokens, n_heads, d_c, d_model, dtype)) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const int K = n_heads * d_c;
-  const int sp = out_splits(n_tokens, n_heads, d_c, d_model, dtype);
   float* P = (float*)workspace;
+  const StreamDesc sd = out_stream(out_lat, a_vo, P, n_tokens, n_heads, d_c, d_model, dtype);
+  if (sd.splits > 0 && stream_gemm_ok(sd)) {
+    MLA_TRY(launch_stream_gemm(sd, s));
+    return launch_splitk_reduce(P, sd.splits, sd.p_split, d_model, out, d_model, (int)n_tokens, d_model, dtype, s);
+  }
+  const int sp = out_splits(n_tokens, n_heads, d_c, d_model, dtype);
   // out[n, i] = sum over heads and latent dims of a_vo[i, (h, j)] out_lat[n, h, j]: the head sum is the contraction
   GemmDesc g = gemm(out_lat, K, a_vo, K, P, d_model, (int)n_tokens, d_model, K, dtype);
   g.out_f32 = true;

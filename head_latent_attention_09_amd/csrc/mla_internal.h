@@ -242,6 +242,22 @@ int launch_gemm_nt(const GemmDesc& g, hipStream_t s);
 // of 64, N a multiple of 8, 16-byte aligned rows
 int launch_gemm_pair(const void* A, int64_t lda, const void* B1, const void* B2, int64_t ldb, int n1, int n2,
                      void* C, int64_t ldc, int M, int N, int K, hipStream_t s);
+// C[m, n] = sum_k X[m, k] W[n, k] for at most 64 rows of X against a weight
+// stream (see mla_stream.hip); bf16 inputs, fp32 partials P[split][M][N]
+// out (K a multiple of 256).
+struct StreamDesc {
+  const void* X;
+  int64_t ldx;
+  const void* W;
+  int64_t ldw;
+  float* P;
+  int64_t p_split;
+  int M, N, K, splits;
+};
+bool stream_gemm_ok(const StreamDesc& d);
+// split count that fills `cus` compute units with one workgroup each, at most max_splits
+int stream_gemm_splits(int N, int K, int cus, int max_splits);
+int launch_stream_gemm(const StreamDesc& d, hipStream_t s);
 int launch_splitk_reduce(const float* P, int splits, int64_t split_stride, int64_t ldp, void* C, int64_t ldc, int M,
                          int N, int dtype, hipStream_t s);
 int launch_transpose(const void* in, void* out, int rows, int cols, int batch, int64_t in_batch, int64_t out_batch,

@@ -85,6 +85,7 @@ def _append_case(dtype, N, d_model, d_c, d_r, paged, seed, n_seqs=4, page=64, ba
 
 @pytest.mark.parametrize("dtype,N,d_model,d_c,d_r,paged", [
     (G.BF16, 64, 5120, 512, 64, True),      # one decode token per sequence, DeepSeek-V2 widths (split-K MFMA)
+    (G.BF16, 37, 2048, 512, 64, False),     # ragged token count, 16 K splits of two 64-wide slices
     (G.BF16, 300, 1024, 512, 64, False),    # a prefill chunk, dense cache
     (G.F32, 9, 100, 20, 4, True),           # fp32, widths off the MFMA tiles (generic product)
 ])
@@ -282,6 +283,40 @@ def test_full_absorption_bf16():
         e = rel_err(out[b], ref)
         say(f"  seq {b} len {lens[b]}: final rel err {e:.2e}")
         assert e <= TOL[G.BF16]
+
+
+@pytest.mark.parametrize("H,d_cq,d_model,N", [
+    (64, 768, 1000, 37),   # output: 4 row tiles (the last ragged) x 64 K splits of 2 blocks (one block pair)
+    (64, 1280, 256, 64),   # 64 tokens (the stream's largest), one output row tile
+    (8, 1536, 5120, 5),    # output: 20 row tiles x 12 splits of 1-2 blocks (the tail-only block path)
+])
+def test_full_absorption_weight_stream(H, d_cq, d_model, N):
+    """Decode-sized fully absorbed layer (bf16): the head-summed output of at
+    most 64 tokens runs on the weight-streaming kernel. The latent output of
+    every token against the oracle's absorbed decode (checks the query), then
+    the layer output."""
+    rng = np.random.default_rng(40 + H + N)
+    dc, dr = 512, 64
+    aqk_d, aqk = stored(rnd(rng, (H, dc, d_cq), 1 / math.sqrt(d_cq)), G.BF16)
+    avo_d, avo = stored(rnd(rng, (d_model, H * dc), 1 / math.sqrt(H * dc)), G.BF16)
+    cq_d, cq = stored(rnd(rng, (N, d_cq)), G.BF16)
+    qp_d, qp = stored(rnd(rng, (N, H, dr)), G.BF16)
+    lens = [int(x) for x in rng.integers(1, 40, N)]
+    case = G.decode_case(N, H, dc, dr, lens, G.BF16, seed=43, poison=False)
+    scale = 1.0 / math.sqrt(128 + dr)
+    q = M.absorb_q_full(cq_d, qp_d, aqk_d)
+    lat, _ = M.latent_decode(q, to_dev(case.cache, G.BF16), torch.tensor(lens, dtype=torch.int32).cuda(), dc,
+                             scale)
+    out = to_host64(M.out_absorbed(lat, avo_d))
+    lat_h = to_host64(lat)
+    e_lat = e_out = 0.0
+    for b in range(N):
+        latb = G.to_f64(G.seq_rows(case, b), G.BF16)
+        ref, ref_lat = O.full_absorbed_decode(cq[b], qp[b], latb, dc, aqk, avo, scale, lens[b])
+        e_lat = max(e_lat, rel_err(lat_h[b], ref_lat))
+        e_out = max(e_out, rel_err(out[b], ref))
+    say(f"H={H} d_cq={d_cq} d_model={d_model} N={N}: latent {e_lat:.2e} output {e_out:.2e}")
+    assert e_lat <= TOL[G.BF16] and e_out <= TOL[G.BF16]
 
 
 # ----------------------------------------------------------------------------
