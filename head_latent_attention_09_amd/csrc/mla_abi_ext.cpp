@@ -7,6 +7,8 @@
 
 #include "mla_internal.h"
 
+#include <initializer_list>
+
 using namespace mla;
 
 namespace {
@@ -77,6 +79,18 @@ StreamDesc out_stream(const void* out_lat, const void* a_vo, float* P, int64_t n
   const int cap = out_splits(n_tokens, n_heads, d_c, d_model, dtype);
   d.splits = stream_gemm_splits(d_model, K, kCuRef, cap);
   return d;
+}
+
+// The gated layer's products on 256 x 256 tiles: they pay off once they fill
+// the chip (at least one tile per CU for an output of n rows and 2 d_model
+// columns); contractions over d_model and the latent width in whole 64-wide
+// slices, every operand 16-byte aligned (bf16 only, checked by the caller).
+bool pair_fits(int64_t n, int d_model, int latent, std::initializer_list<const void*> ptrs) {
+  if (n < 256 || (n / 256) * ((2 * (int64_t)d_model) / 256) < kCuRef) return false;
+  if (d_model % 64 || latent % 64) return false;
+  for (const void* p : ptrs)
+    if ((uintptr_t)p & 15) return false;
+  return true;
 }
 
 bool gated_flash_route(int d_model, int n_heads, int dtype) {
@@ -398,11 +412,48 @@ int mla_gated_mla(const void* x, const void* w_q, const void* w_c, const void* w
   void* Ot = ws + 2 * nd;   // the head contexts (then gated)
   void* V = ws + 3 * nd;    // values (flash route) / scratch
   char* rest = ws + 4 * nd;
-  // Q = X W_q^T, C = X W_c^T (the returned latent cache), gate pre-activations X W_g^T
-  MLA_TRY(launch_gemm_nt(gemm(x, D, w_q, D, Q, D, (int)n, D, D, dtype), s));
-  MLA_TRY(launch_gemm_nt(gemm(x, D, w_c, D, latent_cache, L, (int)n, L, D, dtype), s));
-  MLA_TRY(launch_gemm_nt(gemm(x, D, w_g, D, Gt, D, (int)n, D, D, dtype), s));
   const float scale = 1.0f / std::sqrt((float)Dh);
+  // C = X W_c^T (the returned latent cache)
+  MLA_TRY(launch_gemm_nt(gemm(x, D, w_c, D, latent_cache, L, (int)n, L, D, dtype), s));
+  if (gated_flash_route(D, n_heads, dtype) && pair_fits(n, D, L, {x, w_q, w_g, w_k, w_v, w_o, out, latent_cache})) {
+    // Large products on 256 x 256 tiles: [Q | G] = X [W_q ; W_g]^T in one product (row t =
+    // [q_t | g_t], over the Q and G regions, which are adjacent), [K | V] = C [W_k ; W_v]^T
+    // likewise (over the V and K regions), then attention per head with the gate fused,
+    // reading Q, G, K and V through their row strides
+    void* QG = Q;
+    void* KV = V;
+    MLA_TRY(launch_gemm_pair(x, D, w_q, w_g, D, D, D, QG, 2 * D, (int)n, 2 * D, D, s));
+    MLA_TRY(launch_gemm_pair(latent_cache, L, w_k, w_v, L, D, D, KV, 2 * D, (int)n, 2 * D, L, s));
+    FlashDesc f{};
+    f.q = QG;
+    f.q_row = 2 * D;
+    f.q_head = Dh;
+    f.k = KV;
+    f.k_row = 2 * D;
+    f.k_head = Dh;
+    f.v = (char*)KV + (size_t)D * es;
+    f.v_row = 2 * D;
+    f.v_head = Dh;
+    f.o = Ot;
+    f.o_row = D;
+    f.o_head = Dh;
+    f.gate = (char*)QG + (size_t)D * es;
+    f.g_row = 2 * D;
+    f.g_head = Dh;
+    f.B = batch;
+    f.S_q = seq;
+    f.S_kv = seq;
+    f.H = n_heads;
+    f.d_r = 0;
+    f.scale = scale;
+    f.causal = causal != 0;
+    MLA_TRY(launch_flash(f, s));
+    // Y = (sigmoid(G) * O~) W_o^T
+    return launch_gemm_pair(Ot, D, w_o, nullptr, D, D, 0, out, D, (int)n, D, D, s);
+  }
+  // Q = X W_q^T, gate pre-activations X W_g^T
+  MLA_TRY(launch_gemm_nt(gemm(x, D, w_q, D, Q, D, (int)n, D, D, dtype), s));
+  MLA_TRY(launch_gemm_nt(gemm(x, D, w_g, D, Gt, D, (int)n, D, D, dtype), s));
   if (gated_flash_route(D, n_heads, dtype)) {
     // K = C W_k^T, V = C W_v^T per position, then attention per head with the gate fused
     void* K = rest;

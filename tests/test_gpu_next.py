@@ -340,6 +340,7 @@ def test_gated_worked_example_on_gpu(golden_dir):
     (G.BF16, 2, 200, 256, 64, 2, True),     # D_h = 128: per-head attention over expanded K, V, gate fused
     (G.BF16, 2, 200, 256, 64, 2, False),
     (G.BF16, 1, 150, 256, 96, 4, True),     # D_h = 64: the absorbed latent route
+    (G.BF16, 1, 4096, 2048, 512, 16, True), # projections on 256 x 256 tiles ([Q | G] and [K | V] in one product each)
     (G.F32, 1, 3, 2, 1, 2, False),          # the page's second shape example
     (G.F32, 1, 2, 2, 1, 1, True),           # the page's first shape example
     (G.F32, 2, 33, 24, 8, 3, True),
