@@ -35,9 +35,15 @@ def _flags():
             "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+# Per-source flags. The attention kernels of mla_flash.hip never produce or
+# test NaN (masked scores are -inf, not NaN): without NaN semantics the
+# maximum of raw MFMA scores needs no quieting instruction per operand.
+EXTRA = {"mla_flash.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, obj_dir: str) -> str:
     obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + _flags() + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -27,6 +27,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace mla {
 namespace fa {
 
@@ -210,14 +212,20 @@ __global__ __launch_bounds__(NT, 2) void flash_kernel(Args a) {
         }
       }
       // ---- online softmax. Lane holds key 32 mb + 8 (r / 4) + 4 g + r % 4 of
-      // its query. A full block (every key visible) with a positive scale
-      // takes the maximum of the raw scores and folds the scale into one
-      // fused multiply-add per weight; diagonal and tail blocks scale, mask
-      // and take the maximum of the scaled scores (then sc = 1).
+      // its query. The scores are never rewritten (a rewrite on some blocks
+      // only makes the compiler copy all 32 of them on every block): a full
+      // block (every key visible) with a positive scale takes the maximum of
+      // the raw scores and scales it; other blocks take the maximum of the
+      // scaled visible scores; the scale is folded into the exponent's
+      // multiply-add, and on those blocks invisible keys get weight 0.
       const bool full = k0 + KB <= a.S_kv && (!CAUSAL || k0 + KB - 1 <= qw0 + off);
       const bool fast = full && a.scale_log2 > 0.f;  // wave-uniform
+      const float sc = a.scale_log2;
+      auto visible = [&](int mb, int r) {
+        const int kk = k0 + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
+        return kk < a.S_kv && (!CAUSAL || kk <= qi + off);
+      };
       float mx;
-      float sc = a.scale_log2;
       if (fast) {
         float m0 = fmaxf(s[0][0], s[0][1]), m1 = fmaxf(s[1][0], s[1][1]);
 #pragma unroll
@@ -231,14 +239,8 @@ __global__ __launch_bounds__(NT, 2) void flash_kernel(Args a) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kk = k0 + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool ok = kk < a.S_kv && (!CAUSAL || kk <= qi + off);
-            const float x = ok ? s[mb][r] * sc : -INFINITY;
-            s[mb][r] = x;
-            mx = fmaxf(mx, x);
-          }
-        sc = 1.f;
+          for (int r = 0; r < 16; ++r)
+            if (visible(mb, r)) mx = fmaxf(mx, s[mb][r] * sc);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       // The reference moves only when the maximum rises by more than 8 (log2
@@ -252,26 +254,37 @@ __global__ __launch_bounds__(NT, 2) void flash_kernel(Args a) {
       m_run = m_next;
       bf16x8 pf[4];  // B operand of the value MFMA for key k-steps 0..3
       float psum = 0.f;
-      const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+      // two copies of the weight loop, chosen once per block: without and with the mask
+      auto weights = [&](auto mask_c) {
+        constexpr bool MASK = decltype(mask_c)::value;
+        const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          bf16x8 p8;
+          for (int jj = 0; jj < 2; ++jj) {
+            bf16x8 p8;
 #pragma unroll
-          for (int t = 0; t < 8; t += 2) {
-            const float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][8 * jj + t], sc, -m_use));
-            const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][8 * jj + t + 1], sc, -m_use));
-            bf16x2 q2;
-            q2[0] = f32_to_bf16(w0);
-            q2[1] = f32_to_bf16(w1);
-            p8[t] = q2[0];
-            p8[t + 1] = q2[1];
-            // the denominator sums exactly the rounded weights the MFMA uses
-            psum = __builtin_amdgcn_fdot2_f32_bf16(q2, ones, psum, false);
+            for (int t = 0; t < 8; t += 2) {
+              const int r0 = 8 * jj + t, r1 = r0 + 1;
+              float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r0], sc, -m_use));
+              float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r1], sc, -m_use));
+              if (MASK) {
+                w0 = visible(mb, r0) ? w0 : 0.f;
+                w1 = visible(mb, r1) ? w1 : 0.f;
+              }
+              bf16x2 q2;
+              q2[0] = f32_to_bf16(w0);
+              q2[1] = f32_to_bf16(w1);
+              p8[t] = q2[0];
+              p8[t + 1] = q2[1];
+              // the denominator sums exactly the rounded weights the MFMA uses
+              psum = __builtin_amdgcn_fdot2_f32_bf16(q2, ones, psum, false);
+            }
+            pf[2 * mb + jj] = p8;
           }
-          pf[2 * mb + jj] = p8;
-        }
+      };
+      if (fast) weights(std::false_type{});
+      else weights(std::true_type{});
       l_run = l_run * alpha + psum;
       if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
