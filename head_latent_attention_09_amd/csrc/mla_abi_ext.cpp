@@ -147,13 +147,19 @@ int mla_cache_append(const void* x, const void* w_c, const void* w_kr, const voi
   const int splits = append_splits(n_tokens, d_model, d_c, dtype);
   float* P = (float*)workspace;
   const int64_t sstride = (int64_t)n_tokens * W;
-  // [z_c | z_r] = x [W_c ; W_kr]^T as fp32 partial sums (split over the model width)
+  // [z_c | z_r] = x [W_c ; W_kr]^T as fp32 partial sums (split over the model width): one
+  // product reading W_c and W_kr as one weight where the MFMA path takes it, else two
   GemmDesc g = gemm(x, d_model, w_c, d_model, P, W, n_tokens, d_c, d_model, dtype);
   g.out_f32 = true;
   g.splits = splits;
   g.c_split = sstride;
-  MLA_TRY(launch_gemm_nt(g, s));
-  if (d_r > 0) {
+  GemmDesc gf = g;
+  gf.N = W;
+  gf.B2 = w_kr;
+  gf.n1 = d_c;
+  const bool one = d_r > 0 && gemm_nt_mfma_ok(gf);
+  MLA_TRY(launch_gemm_nt(one ? gf : g, s));
+  if (d_r > 0 && !one) {
     GemmDesc gr = gemm(x, d_model, w_kr, d_model, P + d_c, W, n_tokens, d_r, d_model, dtype);
     gr.out_f32 = true;
     gr.splits = splits;

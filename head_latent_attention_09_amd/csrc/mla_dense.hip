@@ -45,8 +45,10 @@ __device__ __forceinline__ void barrier() {
 
 template <typename OutT>
 struct GemmArgs {
-  const bf16* A;  // A[batch * a_batch + m * lda + k]
-  const bf16* B;  // B[batch * b_batch + n * ldb + k]
+  const bf16* A;   // A[batch * a_batch + m * lda + k]
+  const bf16* B;   // B[batch * b_batch + n * ldb + k] for n < n1,
+  const bf16* B2;  // B2[batch * b_batch + (n - n1) * ldb + k] for n >= n1 (two weights read as one)
+  int n1;
   OutT* C;        // C[batch * c_batch + split * c_split + m * ldc + n]
   int64_t lda, ldb, ldc, a_batch, b_batch, c_batch, c_split;
   int M, N, K;
@@ -56,8 +58,11 @@ struct GemmArgs {
 // Loads of one stage: A and B 128 rows x 8 chunks each, 4 + 4 loads of 64
 // lanes per wave. Rows past M (N) re-read the last valid row (finite data;
 // those outputs are not stored).
-__device__ __forceinline__ void issue_rows(const bf16* base, int64_t ld, int row0, int nrows, int k0, char* dst,
-                                           int lane, int wv) {
+// Loads of one stage: A and B 128 rows x 8 chunks each, 4 + 4 loads of 64
+// lanes per wave. Rows past M (N) re-read the last valid row (finite data;
+// those outputs are not stored). Rows from n1 on come from base2.
+__device__ __forceinline__ void issue_rows(const bf16* base, const bf16* base2, int n1, int64_t ld, int row0,
+                                           int nrows, int k0, char* dst, int lane, int wv) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ld_i = wv * 4 + i;
@@ -66,7 +71,7 @@ __device__ __forceinline__ void issue_rows(const bf16* base, int64_t ld, int row
     const int c = (p & 7) ^ swz8(row);
     int r = row0 + row;
     r = r < nrows ? r : nrows - 1;
-    const bf16* src = base + (int64_t)r * ld + k0 + c * 8;
+    const bf16* src = (r < n1 ? base + (int64_t)r * ld : base2 + (int64_t)(r - n1) * ld) + k0 + c * 8;
     __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(dst + ld_i * 1024), 16, 0, 0);
   }
 }
@@ -84,6 +89,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_nt_kernel(GemmArgs<OutT> a) {
   const int nk = min(nk_all - kc0, a.kps);
   const bf16* A = a.A + batch * a.a_batch;
   const bf16* B = a.B + batch * a.b_batch;
+  const bf16* B2 = a.B2 + batch * a.b_batch;
   OutT* C = a.C + batch * a.c_batch + split * a.c_split;
 
   f32x16 acc[2][2];
@@ -93,8 +99,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_nt_kernel(GemmArgs<OutT> a) {
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   auto issue = [&](int kc, char* st) {
-    issue_rows(A, a.lda, m0, a.M, (kc0 + kc) * BK, st, lane, wv);
-    issue_rows(B, a.ldb, n0, a.N, (kc0 + kc) * BK, st + A_BYTES, lane, wv);
+    issue_rows(A, A, a.M, a.lda, m0, a.M, (kc0 + kc) * BK, st, lane, wv);
+    issue_rows(B, B2, a.n1, a.ldb, n0, a.N, (kc0 + kc) * BK, st + A_BYTES, lane, wv);
   };
   if (nk > 0) issue(0, smem);
   if (nk > 1) issue(1, smem + STAGE_BYTES);
@@ -508,7 +514,7 @@ static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 bool gemm_nt_mfma_ok(const GemmDesc& g) {
   return g.dtype == MLA_BF16 && g.K % dn::BK == 0 && g.K > 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
-         g.a_batch % 8 == 0 && g.b_batch % 8 == 0 && al16(g.A) && al16(g.B) &&
+         g.a_batch % 8 == 0 && g.b_batch % 8 == 0 && al16(g.A) && al16(g.B) && (!g.B2 || al16(g.B2)) &&
          (g.out_f32 || (g.N % 8 == 0 && g.ldc % 8 == 0 && g.c_batch % 8 == 0 && al16(g.C)));
 }
 
@@ -530,6 +536,10 @@ int launch_gemm_pair(const void* A, int64_t lda, const void* B1, const void* B2,
 
 int launch_gemm_nt(const GemmDesc& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return MLA_OK;
+  // a second weight (rows from n1 on) only on the MFMA path
+  if (g.B2 && (g.n1 < 0 || !gemm_nt_mfma_ok(g))) return MLA_ERR_UNSUPPORTED;
+  const bf16* B2 = g.B2 ? (const bf16*)g.B2 : (const bf16*)g.B;
+  const int n1 = g.B2 ? g.n1 : g.N;
   if (gemm_nt_mfma_ok(g)) {
     const int nk = g.K / dn::BK;
     const int splits = g.splits < 1 ? 1 : (g.splits > nk ? nk : g.splits);
@@ -537,12 +547,12 @@ int launch_gemm_nt(const GemmDesc& g, hipStream_t s) {
     dim3 grid((unsigned)((g.M + dn::BM - 1) / dn::BM), (unsigned)((g.N + dn::BN - 1) / dn::BN),
               (unsigned)(g.batch * splits));
     if (g.out_f32) {
-      dn::GemmArgs<float> a{(const bf16*)g.A, (const bf16*)g.B, (float*)g.C, g.lda, g.ldb, g.ldc,
+      dn::GemmArgs<float> a{(const bf16*)g.A, (const bf16*)g.B, B2, n1, (float*)g.C, g.lda, g.ldb, g.ldc,
                             g.a_batch, g.b_batch, g.c_batch, g.c_split, g.M, g.N, g.K, splits, kps};
       hipLaunchKernelGGL(dn::gemm_nt_kernel<float>, grid, dim3(dn::NT), 0, s, a);
     } else {
       if (splits != 1) return MLA_ERR_UNSUPPORTED;
-      dn::GemmArgs<bf16> a{(const bf16*)g.A, (const bf16*)g.B, (bf16*)g.C, g.lda, g.ldb, g.ldc,
+      dn::GemmArgs<bf16> a{(const bf16*)g.A, (const bf16*)g.B, B2, n1, (bf16*)g.C, g.lda, g.ldb, g.ldc,
                            g.a_batch, g.b_batch, g.c_batch, 0, g.M, g.N, g.K, 1, kps};
       hipLaunchKernelGGL(dn::gemm_nt_kernel<bf16>, grid, dim3(dn::NT), 0, s, a);
     }

@@ -226,6 +226,8 @@ inline bool abi_aligned(const void* p, int a) { return ((uintptr_t)p % (uintptr_
 struct GemmDesc {
   const void* A;
   const void* B;
+  const void* B2;  // optional: rows n >= n1 of the weight come from B2 (MFMA path only)
+  int n1;
   void* C;
   int64_t lda, ldb, ldc;
   int64_t a_batch, b_batch, c_batch, c_split;
