@@ -104,12 +104,24 @@ __global__ __launch_bounds__(NT, 2) void flash_kernel(Args a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, l32 = lane & 31;
 
-  // heaviest query blocks first (causal), (sequence, head) fastest: workgroups
-  // of one (sequence, head) sit H*B apart, on the same XCD when H*B % 8 == 0
+  // Workgroup i runs on XCD i % 8. With many (sequence, head) pairs (a multiple of 8, at
+  // least 16 per XCD), every query block of one pair goes to the same XCD and they are
+  // dispatched back to back (heaviest first), so the blocks that stream that pair's keys and
+  // values run together and share them through that XCD's L2 (measured 4.6 % faster at
+  // B=2, H=128, S=4096). With few pairs (their keys and values fit the last-level cache
+  // anyway) that order leaves XCDs unevenly loaded at the end (3 % slower at B=2, H=16):
+  // heaviest query blocks first, (sequence, head) fastest.
   const int BH = a.B * a.H;
   const int id = blockIdx.x;
-  const int qb = a.nqb - 1 - id / BH;
-  const int bh = id % BH;
+  int qb, bh;
+  if (BH % 8 == 0 && BH >= 128) {
+    const int xcd = id & 7, local = id >> 3;
+    qb = a.nqb - 1 - local % a.nqb;
+    bh = (local / a.nqb) * 8 + xcd;
+  } else {
+    qb = a.nqb - 1 - id / BH;
+    bh = id % BH;
+  }
   const int b = bh / a.H, h = bh - b * a.H;
   const int q0 = qb * QB;
   const int off = a.S_kv - a.S_q;  // query i sees keys t <= i + off (causal)
