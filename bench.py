@@ -33,7 +33,6 @@ its softmax (--headline-only skips them; --skip-headline runs only them,
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -75,29 +74,6 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
-
-
-def src_hash(path):
-    """SHA-256 prefix of a kernel source with its // comments and blank lines
-    removed, so that counter results survive edits of the comments only."""
-    import re
-    with open(path) as f:
-        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in f]
-    code = "\n".join(ln for ln in lines if ln)
-    return hashlib.sha256(code.encode()).hexdigest()[:16]
-
-
-def traffic_from_profile(per_launch_alg_bytes):
-    """Measured HBM bytes per attention launch from committed counter runs,
-    valid only for the kernel source they were taken on."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("kernel_source_sha256_16") != src_hash(ATTN_SRC):
-        return None
-    return t.get("bytes_per_launch")
 
 
 def cpu_baseline(case, budget_s):
@@ -231,7 +207,8 @@ def main():
     alg_bytes = B * S * W * ESIZE + B * H * W * ESIZE + B * H * D_C * ESIZE   # cache + queries + latent output
     alg_flop = B * S * H * (2 * W + 2 * D_C)                   # QK (576) + PV (512) per head-position
     achieved = alg_bytes / (attn_avg / 1e3) / 1e9
-    traffic = traffic_from_profile(alg_bytes)
+    import bench_workloads as BW
+    traffic = BW.traffic_from_profile(TRAFFIC_FILE, ATTN_SRC)
     line = {
         "metric": "latent tokens attended/sec (B*H*seq), H=128 decode",
         "value": round(value, 1),

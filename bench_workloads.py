@@ -11,6 +11,8 @@ generator); timing does not depend on the exact values.
 """
 from __future__ import annotations
 
+import hashlib
+import json
 import math
 import os
 import sys
@@ -20,6 +22,35 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+
+
+PROFILE_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+ATTN_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "head_latent_attention_09_amd", "csrc",
+                        "mla_attn.hip")
+RAGGED_TRAFFIC_FILE = os.path.join(PROFILE_DIR, "latent_attention_ragged_paged_b128_h128_traffic.json")
+
+
+def src_hash(path):
+    """SHA-256 prefix of a kernel source with its // comments and blank lines
+    removed, so that counter results survive edits of the comments only."""
+    import re
+    with open(path) as f:
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in f]
+    code = "\n".join(ln for ln in lines if ln)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
+def traffic_from_profile(path, src=ATTN_SRC):
+    """Measured HBM bytes per launch from a committed counter summary, valid
+    only for the kernel source it was taken on (else None)."""
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != src_hash(src):
+        return None
+    return t.get("bytes_per_launch")
 
 
 def log(msg):
@@ -137,7 +168,8 @@ def bench_ragged_paged(M, G, torch, dev, args, time_entry):
            "entry_points_ms": {"latent_decode (attention + combine)": entry},
            "roofline": dict(roof("hbm", alg_bytes, attn / 1e3),
                             kernel="latent attention (mla::mf::attn_mfma_kernel<4, true, true>)",
-                            avg_launch_ms=round(attn, 5), alg_bytes_per_launch=alg_bytes, traffic=None),
+                            avg_launch_ms=round(attn, 5), alg_bytes_per_launch=alg_bytes,
+                            traffic=traffic_from_profile(RAGGED_TRAFFIC_FILE)),
            "roofline_mfma": roof("mfma", tokens * H * (2 * 576 + 2 * 512), attn / 1e3)}
     if not args.no_cpu_baseline:
         # the oracle on whole sequences drawn with the first lengths of the workload
