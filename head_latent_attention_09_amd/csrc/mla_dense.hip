@@ -320,6 +320,76 @@ __global__ __launch_bounds__(256) void cache_rows_kernel(const float* P, int spl
   }
 }
 
+// The same rows with one wave per token (four tokens per workgroup of 256),
+// for rows at most 1024 wide with an even latent width and many tokens: lane l holds
+// elements l, l + 64, ... of the row, the sum of squares is a wave reduction,
+// and the two elements of a rope pair sit in lanes l and l ^ 1 of the same
+// register, so the kernel needs no barrier and no LDS.
+constexpr int CRW_EPT = 16;
+template <typename T>
+__global__ __launch_bounds__(256) void cache_rows_wave_kernel(const float* P, int splits, int64_t split_stride,
+                                                              const T* gain, float eps, double log2_base,
+                                                              const int32_t* seq_ids, const int32_t* positions,
+                                                              T* cache, RowMap map, int n_seqs, int n_tokens, int d_c,
+                                                              int d_r) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= n_tokens) return;  // wave-uniform from here on: one token per wave
+  const int W = d_c + d_r;
+  const int b = seq_ids[n], pos = positions[n];
+  int64_t slot;
+  if (b < 0 || b >= n_seqs || pos < 0) return;
+  if (map.mode == 1) {
+    if (pos >= map.max_pages * map.page_size) return;
+    const int pg = map.block_table[(int64_t)b * map.max_pages + pos / map.page_size];
+    if (pg < 0 || pg >= map.num_pages) return;
+    slot = (int64_t)pg * map.page_size + pos % map.page_size;
+  } else {
+    if (pos >= map.cache_stride) return;
+    slot = (int64_t)b * map.cache_stride + pos;
+  }
+  T* dst = cache + slot * W;
+  const float* src = P + (int64_t)n * W;
+  float v[CRW_EPT];
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < CRW_EPT; ++e) {
+    const int j = lane + 64 * e;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    if (j < W) {
+      int k = 0;
+      for (; k + 4 <= splits; k += 4) {
+        a0 += src[(int64_t)k * split_stride + j];
+        a1 += src[(int64_t)(k + 1) * split_stride + j];
+        a2 += src[(int64_t)(k + 2) * split_stride + j];
+        a3 += src[(int64_t)(k + 3) * split_stride + j];
+      }
+      for (; k < splits; ++k) a0 += src[(int64_t)k * split_stride + j];
+    }
+    v[e] = (a0 + a1) + (a2 + a3);
+    if (j < d_c) ss += v[e] * v[e];
+  }
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float inv = 1.0f / sqrtf(ss / (float)d_c + eps);
+#pragma unroll
+  for (int e = 0; e < CRW_EPT; ++e) {
+    const int j = lane + 64 * e;
+    const float pv = __shfl_xor(v[e], 1);  // the pair partner (every lane takes part)
+    if (j < d_c) {
+      float x = v[e] * inv;
+      if (gain) x *= load_f32(gain + j);
+      store_f32(dst + j, x);
+    } else if (j < W) {
+      // rope element ri = j - d_c of pair i = ri / 2 (d_c even: the partner is element j ^ 1)
+      const int ri = j - d_c;
+      float c, sn;
+      rope_angle(pos, ri >> 1, d_r, log2_base, c, sn);
+      const float y = (ri & 1) ? pv * sn + v[e] * c : v[e] * c - pv * sn;
+      store_f32(dst + j, y);
+    }
+  }
+}
+
 // q[n, h, col0 + 2i .. +1] = rotation of q_pe[n, h, 2i .. +1] at positions[n]
 template <typename T>
 __global__ __launch_bounds__(256) void rope_rows_kernel(const T* src, T* dst, const int32_t* positions, int64_t rows,
@@ -623,6 +693,21 @@ int launch_cache_rows(const float* P, int splits, int64_t split_stride, const vo
                       int n_tokens, int d_c, int d_r, int dtype, hipStream_t s) {
   if (n_tokens <= 0) return MLA_OK;
   const double lb = log2((double)rope_base);
+  // one wave per token once the tokens fill the chip (8192 tokens, 2 splits: 104 -> 96 us);
+  // few tokens with many splits (decode) keep 256 threads per token, whose split sums run
+  // in parallel (64 tokens, 16 splits: 16 against 24 us)
+  if (d_c + d_r <= 64 * dn::CRW_EPT && d_c % 2 == 0 && n_tokens >= 1024) {
+    const dim3 grid((unsigned)((n_tokens + 3) / 4));
+    if (dtype == MLA_BF16)
+      hipLaunchKernelGGL(dn::cache_rows_wave_kernel<bf16>, grid, dim3(256), 0, s, P, splits, split_stride,
+                         (const bf16*)gain, eps, lb, seq_ids, positions, (bf16*)cache, map, n_seqs, n_tokens, d_c,
+                         d_r);
+    else
+      hipLaunchKernelGGL(dn::cache_rows_wave_kernel<float>, grid, dim3(256), 0, s, P, splits, split_stride,
+                         (const float*)gain, eps, lb, seq_ids, positions, (float*)cache, map, n_seqs, n_tokens, d_c,
+                         d_r);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  }
   if (dtype == MLA_BF16)
     hipLaunchKernelGGL(dn::cache_rows_kernel<bf16>, dim3((unsigned)n_tokens), dim3(256), 0, s, P, splits,
                        split_stride, (const bf16*)gain, eps, lb, seq_ids, positions, (bf16*)cache, map, n_seqs, d_c,

@@ -88,6 +88,8 @@ def _append_case(dtype, N, d_model, d_c, d_r, paged, seed, n_seqs=4, page=64, ba
     (G.BF16, 37, 2048, 512, 64, False),     # ragged token count, 16 K splits of two 64-wide slices
     (G.BF16, 300, 1024, 512, 64, False),    # a prefill chunk, dense cache
     (G.F32, 9, 100, 20, 4, True),           # fp32, widths off the MFMA tiles (generic product)
+    (G.F32, 1100, 96, 20, 4, False),        # enough tokens for the wave-per-token row epilogue
+    (G.BF16, 1536, 1024, 512, 64, True),    # the same epilogue at DeepSeek-V2 row widths, paged
 ])
 def test_cache_append(dtype, N, d_model, d_c, d_r, paged):
     say(f"cache append: {dtype} N={N} d_model={d_model} d_c={d_c} d_r={d_r} paged={paged}")
