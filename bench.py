@@ -237,6 +237,8 @@ def main():
         "wall_s_timed": round(wall, 3),
         "entry_points_ms": entry,
     }
+    if not args.headline_only:
+        line["hbm_reference"] = hbm_reference(torch, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     if not args.headline_only:
@@ -245,6 +247,33 @@ def main():
         import bench_workloads as BW
         line["workloads"] = BW.run_all(M, G, torch, dev, args, time_entry)
     print(json.dumps(line), flush=True)
+
+
+def hbm_reference(torch, dev):
+    """What plain library kernels reach on this part, as context for the HBM
+    fractions (which are against the published 8 TB/s): a 1 GiB bf16 sum
+    (reads only) and a 1 GiB device copy (reads + writes), medians of 10."""
+    x = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    y = torch.empty_like(x)
+    res = {}
+    for name, fn, nbytes in (("sum_read", lambda: x.sum(dtype=torch.float32), 1 << 30),
+                             ("copy_read_write", lambda: y.copy_(x), 2 << 30)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        res[name] = {"GB/s": round(nbytes / (ms / 1e3) / 1e9, 1), "ms": round(ms, 4), "bytes": nbytes}
+    del x, y
+    torch.cuda.empty_cache()
+    return res
 
 
 def copy_calibration(torch, dev):

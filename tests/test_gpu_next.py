@@ -287,18 +287,20 @@ def test_full_absorption_bf16():
         assert e <= TOL[G.BF16]
 
 
-@pytest.mark.parametrize("H,d_cq,d_model,N", [
-    (64, 768, 1000, 37),   # output: 4 row tiles (the last ragged) x 64 K splits of 2 blocks (one block pair)
-    (64, 1280, 256, 64),   # 64 tokens (the stream's largest), one output row tile
-    (8, 1536, 5120, 5),    # output: 20 row tiles x 12 splits of 1-2 blocks (the tail-only block path)
+@pytest.mark.parametrize("H,d_cq,d_model,N,dc", [
+    (64, 768, 1000, 37, 512),  # output: 4 row tiles (the last ragged) x 64 K splits of 2 blocks (one block pair)
+    (64, 1280, 256, 64, 512),  # 64 tokens (the stream's largest), one output row tile
+    (8, 1536, 5120, 5, 512),   # output: 20 row tiles x 12 splits of 1-2 blocks (the tail-only block path)
+    (1, 256, 4, 1, 256),       # one token, 4 output rows of one 256-wide K block (one split, one block)
+    (2, 256, 8, 64, 512),      # 64 tokens against 8 output rows, 4 K blocks in 4 splits
 ])
-def test_full_absorption_weight_stream(H, d_cq, d_model, N):
+def test_full_absorption_weight_stream(H, d_cq, d_model, N, dc):
     """Decode-sized fully absorbed layer (bf16): the head-summed output of at
     most 64 tokens runs on the weight-streaming kernel. The latent output of
     every token against the oracle's absorbed decode (checks the query), then
     the layer output."""
     rng = np.random.default_rng(40 + H + N)
-    dc, dr = 512, 64
+    dr = 64
     aqk_d, aqk = stored(rnd(rng, (H, dc, d_cq), 1 / math.sqrt(d_cq)), G.BF16)
     avo_d, avo = stored(rnd(rng, (d_model, H * dc), 1 / math.sqrt(H * dc)), G.BF16)
     cq_d, cq = stored(rnd(rng, (N, d_cq)), G.BF16)
