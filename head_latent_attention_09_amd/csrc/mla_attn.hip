@@ -218,10 +218,14 @@ __device__ void self_plan(const RowMap& m, int R, int G, int tile, int* cum_s, i
 
 // ===========================================================================
 // generic attention (fp32 or bf16 storage, any d_c <= 1024, d_c + d_r <= 1152)
-// fp32 arithmetic on the vector ALUs; 8 heads per workgroup, 16-position tiles.
+// fp32 arithmetic on the vector ALUs; 16 heads per workgroup, 16-position tiles.
 // ===========================================================================
 namespace gn {
 constexpr int TT = 16, HG = 8, WMAX = 1152, DCMAX = 1024, NT = 256;
+// heads per workgroup of the standalone kernel: every tile staged in LDS serves
+// 16 heads (the query block and the tile fill 148 KiB of LDS); the redo inside
+// the MFMA kernel takes 8 at a time in that kernel's smaller scratch
+constexpr int HGK = 16;
 
 template <typename T>
 struct Args {
@@ -235,7 +239,7 @@ struct Args {
   float* lse;
 };
 
-template <typename T>
+template <typename T, int HG>
 __device__ void attend_segment(const Args<T>& a, int r, int len, int lt0, int lt1, bool full, int slot, int h0,
                                float* tile, float* qs, float* ps, float* alpha_s, float* stat_s,
                                float& m_run, float& l_run) {
@@ -314,22 +318,24 @@ __device__ void attend_segment(const Args<T>& a, int r, int len, int lt0, int lt
     stat_s[HG + tid] = (m_run + log2f(l_run)) * kLn2;
   }
   __syncthreads();
+  // (a guard, not a break: the loop unrolls fully, so acc stays in registers)
 #pragma unroll
   for (int hh = 0; hh < HG; ++hh) {
-    if (hh >= nh) break;
-    const int h = h0 + hh;
+    if (hh < nh) {
+      const int h = h0 + hh;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int d = tid + k * NT;
-      if (d < d_c) {
-        float v = acc[hh][k] * stat_s[hh];
-        if (full) store_f32(a.out + ((size_t)r * H + h) * d_c + d, v);
-        else store_f32((T*)a.pl.part_o + ((size_t)slot * H + h) * d_c + d, v);
+      for (int k = 0; k < 4; ++k) {
+        const int d = tid + k * NT;
+        if (d < d_c) {
+          float v = acc[hh][k] * stat_s[hh];
+          if (full) store_f32(a.out + ((size_t)r * H + h) * d_c + d, v);
+          else store_f32((T*)a.pl.part_o + ((size_t)slot * H + h) * d_c + d, v);
+        }
       }
-    }
-    if (tid == 0) {
-      if (full) { if (a.lse) a.lse[(size_t)r * H + h] = stat_s[HG + hh]; }
-      else a.pl.part_lse[(size_t)slot * H + h] = stat_s[HG + hh];
+      if (tid == 0) {
+        if (full) { if (a.lse) a.lse[(size_t)r * H + h] = stat_s[HG + hh]; }
+        else a.pl.part_lse[(size_t)slot * H + h] = stat_s[HG + hh];
+      }
     }
   }
 }
@@ -337,14 +343,14 @@ __device__ void attend_segment(const Args<T>& a, int r, int len, int lt0, int lt
 template <typename T>
 __global__ __launch_bounds__(NT) void attn_generic_kernel(Args<T> a) {
   __shared__ float tile[TT * (WMAX + 1)];
-  __shared__ float qs[HG * WMAX];
-  __shared__ float ps[HG * TT];
-  __shared__ float alpha_s[HG];
-  __shared__ float stat_s[2 * HG];
+  __shared__ float qs[HGK * WMAX];
+  __shared__ float ps[HGK * TT];
+  __shared__ float alpha_s[HGK];
+  __shared__ float stat_s[2 * HGK];
   float m_run = -INFINITY, l_run = 0.f;
   const int G = a.pl.G;
   const int w = xcd_worker(blockIdx.x, G);
-  const int h0 = blockIdx.y * HG;
+  const int h0 = blockIdx.y * HGK;
   const int total = a.pl.cum[a.pl.R];
   const int seg_cost = a.pl.split[1];
   const int per = plan_per_worker(total, G);
@@ -356,8 +362,8 @@ __global__ __launch_bounds__(NT) void attn_generic_kernel(Args<T> a) {
     if (c0 >= t_end) break;
     Segment sg;
     if (!plan_segment(c0, c1, seg_cost, t_begin, t_end, w, per, sg)) continue;
-    attend_segment<T>(a, r, a.pl.len[r], sg.lt0, sg.lt1, sg.full, sg.slot, h0, tile, qs, ps, alpha_s, stat_s, m_run,
-                      l_run);
+    attend_segment<T, HGK>(a, r, a.pl.len[r], sg.lt0, sg.lt1, sg.full, sg.slot, h0, tile, qs, ps, alpha_s, stat_s,
+                           m_run, l_run);
   }
 }
 }  // namespace gn
@@ -619,7 +625,8 @@ __device__ void generic_segment(const Args& a, int r, int len, int lt0, int lt1,
   static_assert((gn::TT * (gn::WMAX + 1) + gn::HG * (gn::WMAX + gn::TT + 3)) * 4 <= SMEM_BYTES, "generic scratch");
   float m_run = -INFINITY, l_run = 0.f;
   for (int h0 = 0; h0 < a.H; h0 += gn::HG)
-    gn::attend_segment<bf16>(ga, r, len, lt0, lt1, full, slot, h0, tile, qs, ps, alpha_s, stat_s, m_run, l_run);
+    gn::attend_segment<bf16, gn::HG>(ga, r, len, lt0, lt1, full, slot, h0, tile, qs, ps, alpha_s, stat_s, m_run,
+                                     l_run);
   __syncthreads();
 }
 
@@ -1276,7 +1283,7 @@ static void launch_generic(const AttnCall& c, const Plan& pl) {
   a.scale_log2 = c.kq_scale * kLog2e;
   a.out = (T*)c.out;
   a.lse = c.lse;
-  dim3 grid(c.G, (c.H + gn::HG - 1) / gn::HG);
+  dim3 grid(c.G, (c.H + gn::HGK - 1) / gn::HGK);
   launch_timed(c, gn::attn_generic_kernel<T>, grid, dim3(gn::NT), a);
 }
 
