@@ -41,7 +41,6 @@ struct L {
   static constexpr int KR = KB * DN * 2;         // key rope rows: 64 x 2*DR B
   static constexpr int VO = KR + KB * DR * 2;    // value rows: 64 x 256 B
   static constexpr int STAGE = VO + KB * DV * 2; // 40 KiB (DR = 64) or 32 KiB (DR = 0)
-  static constexpr int LOADS = (KB * DN * 2 + KB * DR * 2 + KB * DV * 2) / 1024 / NW;  // per wave and stage
 };
 
 struct Args {
@@ -195,12 +194,14 @@ __global__ __launch_bounds__(NT, 2) void flash_kernel(Args a) {
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d) o[d] = f32x16{};
 
+  // two stages, one barrier per block: the barrier that publishes block kb
+  // also proves every wave is done with block kb - 1, whose stage then takes
+  // block kb + 1 while block kb is used
   if (nblk > 0) issue(0, smem);
-  if (nblk > 1) issue(1, smem + Lay::STAGE);
   for (int kb = 0; kb < nblk; ++kb) {
-    if (kb + 1 < nblk) wait_vmcnt<Lay::LOADS>();
-    else wait_vmcnt<0>();
-    barrier();  // block kb is in LDS for every wave
+    wait_vmcnt<0>();
+    barrier();  // block kb is in LDS for every wave; block kb - 1 is no longer read
+    if (kb + 1 < nblk) issue(kb + 1, smem + ((kb + 1) & 1) * Lay::STAGE);
     const char* st = smem + (kb & 1) * Lay::STAGE;
     const int k0 = kb * KB;
     if (k0 < wend) {  // wave-uniform: the wave sees some key of this block
@@ -322,9 +323,8 @@ __global__ __launch_bounds__(NT, 2) void flash_kernel(Args a) {
         }
       }
     }
-    barrier();  // every wave is done with this stage
-    if (kb + 2 < nblk) issue(kb + 2, smem + (kb & 1) * Lay::STAGE);
   }
+  barrier();  // every wave is done with the last block before the stage buffers are reused
 
   // ---- epilogue: normalise, gate, stage through LDS, store whole rows
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(NT, 2) void flash_kernel(Args a) {
     a.lse[((int64_t)b * a.S_q + qi) * a.H + h] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   // wave w stages its 32 queries x 128 dims (8 KiB) at w * 8 KiB; row q16 of
   // the stage: chunk c at c ^ (q & 15)
-  // (the loop's last barrier ended every read of the stage buffers)
+  // (the barrier after the loop ended every read of the stage buffers)
   char* sw = smem + wv * 8192;
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d)
