@@ -413,7 +413,10 @@ constexpr int SMEM_BYTES = LDS_MFIX + 32 * NW * 4;
 // Tile j is loaded into buffer j % NBUF during iteration j - AHEAD, after the
 // barrier that ends every read of the buffer's previous tile j - NBUF (its
 // value fragments are read, and waited for, before the barrier of iteration
-// j - NBUF), and published by the barrier of iteration j - 2.
+// j - NBUF), and published by the barrier of iteration j - 2. Every
+// iteration does the same work: the last ones load and score stand-in tiles
+// past the segment's end (results unused), so the loop has no branches on
+// the tile index and each wave has the same loads in flight at every wait.
 //
 // LDS layouts (XOR swizzles; chosen with the LDS bank-conflict counter on
 // this chip, since its banking is not a plain 4-byte interleave: the score
@@ -454,9 +457,10 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 // copies them back right before the MFMA). With 128 heads every AGPR holds the
 // output and no such copy is made; a CPU test scans the generated code of
 // every instantiation for a VALU write of an operand within two wait states
-// of an unguarded MFMA. After the chain: sync_scores, which the accumulators
-// pass through, so that no read of the result is placed before the wait
-// states it needs.
+// of an unguarded MFMA. After the chain: the last k-step's two MFMAs and the
+// wait states a read of their results needs are one asm block (mfma16_last),
+// so no instruction the compiler places after it, a register copy included,
+// can read a result too early.
 template <bool GUARD>
 __device__ __forceinline__ void mfma16(f32x4& acc, const bf16x8& a, const bf16x8& b) {
   if (GUARD)
@@ -465,14 +469,27 @@ __device__ __forceinline__ void mfma16(f32x4& acc, const bf16x8& a, const bf16x8
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 template <bool GUARD>
+__device__ __forceinline__ void mfma16_last(f32x4& c0, f32x4& c1, const bf16x8& a, const bf16x8& b0,
+                                            const bf16x8& b1) {
+  if (GUARD)
+    asm volatile(
+        "s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %2, %3, %0\n\tv_mfma_f32_16x16x32_bf16 %1, %2, %4, %1\n\t"
+        "s_nop 7\n\ts_nop 7\n\ts_nop 3"
+        : "+v"(c0), "+v"(c1)
+        : "v"(a), "v"(b0), "v"(b1));
+  else
+    asm volatile(
+        "v_mfma_f32_16x16x32_bf16 %0, %2, %3, %0\n\tv_mfma_f32_16x16x32_bf16 %1, %2, %4, %1\n\t"
+        "s_nop 7\n\ts_nop 7\n\ts_nop 3"
+        : "+v"(c0), "+v"(c1)
+        : "v"(a), "v"(b0), "v"(b1));
+}
+template <bool GUARD>
 __device__ __forceinline__ void mfma16_first(f32x4& acc, const bf16x8& a, const bf16x8& b) {
   if (GUARD)
     asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
   else
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void sync_scores(f32x4& a, f32x4& b) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(a), "+v"(b)::"memory");
 }
 
 // Direct global->LDS load of 64 lanes x 16 bytes: lane l reads 16 bytes at
@@ -520,21 +537,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// vmcnt wait with a run-time count: a jump table of immediate waits (counts
-// above 63 wait for 63, which waits for more than asked)
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-#define MLA_W(k) \
-  case k:        \
-    wait_vmcnt<k>(); \
-    break;
-#define MLA_W8(k) MLA_W(k) MLA_W(k + 1) MLA_W(k + 2) MLA_W(k + 3) MLA_W(k + 4) MLA_W(k + 5) MLA_W(k + 6) MLA_W(k + 7)
-    MLA_W8(0) MLA_W8(8) MLA_W8(16) MLA_W8(24) MLA_W8(32) MLA_W8(40) MLA_W8(48) MLA_W8(56)
-#undef MLA_W8
-#undef MLA_W
-    default:
-      wait_vmcnt<63>();
-  }
+// vmcnt wait for the tile loads issued after the one being waited for:
+// AHEAD - 2 tiles of this wave's loads (5 for waves 0 and 1, 4 for the others)
+// plus EXTRA later loads
+template <int EXTRA>
+__device__ __forceinline__ void wait_tiles(int wv) {
+  if (wv < 2)
+    wait_vmcnt<(AHEAD - 2) * 5 + EXTRA>();
+  else
+    wait_vmcnt<(AHEAD - 2) * 4 + EXTRA>();
 }
 
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
@@ -578,8 +589,6 @@ __device__ __forceinline__ TileSrc tile_src(const Args& a, int b, int t0, int le
 // another, so the two rope loads are not split four ways). Rows past the last
 // visible one re-read it (finite data; their weights are zeroed). lx is
 // lane ^ sC(wv): sC(wv + 4k) = sC(wv) ^ sC(4k).
-__device__ __forceinline__ int loads_per_tile(int wv) { return wv < 2 ? 5 : 4; }
-
 template <bool STREAM>
 __device__ __forceinline__ void issue_load(const TileSrc& s, char* buf, int k, int lx, int lane, int wv) {
   if (k < 4) {
@@ -650,11 +659,19 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
   // the compiler's waits for the query registers.
   const int wq = owner ? wv : 0;
   const int ntiles = lt1 - lt0;
-  const int L = loads_per_tile(wv);
   char* const qr_lds = smem + LDS_QR + wv * QR_BYTES;
   float* const inv_s = (float*)(smem + LDS_INV);
   float* const m_fix_s = (float*)(smem + LDS_MFIX);
   auto tbuf = [&](int j) { return smem + (j % NBUF) * TILE_BYTES; };
+  // Source of tile j of the segment. Past the segment's end the pipeline
+  // still loads a tile, so that every step has the same loads in flight and
+  // runs without branches: row 0 of the segment's last tile (a visible row)
+  // into every row, into a buffer whose scores are never used.
+  auto src_of = [&](int j) {
+    TileSrc s = tile_src(a, b, (lt0 + (j < ntiles ? j : ntiles - 1)) * TILE, len);
+    if (j >= ntiles) s.last = s.lastb = 0;
+    return s;
+  };
 
   // every wave must be done with the previous segment's LDS (and flag)
   block_barrier();
@@ -668,8 +685,7 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
     int ln = lane;  // per-lane offsets stay in this segment's code (see the tile loop)
     opaque(ln);
     const int lx = ln ^ sC(wv);
-    const int np = ntiles < AHEAD ? ntiles : AHEAD;
-    for (int j = 0; j < (np < 2 ? np : 2); ++j) issue_tile<STREAM>(tile_src(a, b, (lt0 + j) * TILE, len), tbuf(j), lx, ln, wv);
+    for (int j = 0; j < 2; ++j) issue_tile<STREAM>(src_of(j), tbuf(j), lx, ln, wv);
     {
       const char* qbase = (const char*)(a.q + ((size_t)r * H + wq * 32) * WD + 32 * KQ);
       constexpr int QC = QR_ROW / 16;  // 16-byte slots per row, the last two padding
@@ -681,7 +697,7 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
         dma16(qbase, (uint32_t)(hr * (WD * 2) + (pc << 4)), lds_addr(qr_lds + k * 1024));
       }
     }
-    for (int j = 2; j < np; ++j) issue_tile<STREAM>(tile_src(a, b, (lt0 + j) * TILE, len), tbuf(j), lx, ln, wv);
+    for (int j = 2; j < AHEAD; ++j) issue_tile<STREAM>(src_of(j), tbuf(j), lx, ln, wv);
     {
       const bf16* qrow = a.q + ((size_t)r * H + wq * 32 + (ln & 15)) * WD + (ln >> 4) * 8;
 #pragma unroll
@@ -691,7 +707,7 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
     }
     // tiles 0, 1 and the query rope dims complete; the later tiles and the
     // query registers (waited for by the compiler) may be in flight
-    wait_vm((np > 2 ? np - 2 : 0) * L + 2 * KQ);
+    wait_tiles<2 * KQ>(wv);
   }
   block_barrier();
 
@@ -787,6 +803,8 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
       if (ks == 0) {
         mfma16_first<(NHB < 4)>(acc[0], a_op, b0);
         mfma16_first<(NHB < 4)>(acc[1], a_op, b1);
+      } else if (ks == KS - 1) {
+        mfma16_last<(NHB < 4)>(acc[0], acc[1], a_op, b0, b1);
       } else {
         mfma16<(NHB < 4)>(acc[0], a_op, b0);
         mfma16<(NHB < 4)>(acc[1], a_op, b1);
@@ -804,7 +822,6 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
   // first tile's scores and the segment's reference max
   kprefetch(0);
   scores(0, s0, [](int) {});
-  sync_scores(s0[0], s0[1]);
   {
     const int nvalid = len - lt0 * TILE;
 #pragma unroll
@@ -821,25 +838,21 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
       for (int hb = 0; hb < 2; ++hb) m_ref[hb] = m_fix_s[wv * 32 + hb * 16 + t16] * kLog2e + 1.f;
     }
   }
-  if (owner && ntiles > 1) kprefetch(TILE_BYTES);
+  if (owner) kprefetch(TILE_BYTES);
 
   // One pipeline step (tile it, scores in sc; scores of tile it+1 into sn).
   auto step = [&](int it, f32x4* sc, f32x4* sn) {
     const int boff = (it % NBUF) * TILE_BYTES;
     const int nvalid = len - (lt0 + it) * TILE;  // positions < nvalid of this tile are visible
-    const bool pre = it + AHEAD < ntiles;        // tile it+AHEAD is loaded during this step
-    TileSrc ns = {nullptr, 0};
-    if (pre) {
-      ns = tile_src(a, b, (lt0 + it + AHEAD) * TILE, len);
-      // materialise the (possibly table-derived) source now: a scalar-load
-      // wait later would also drain the operand reads in flight
-      asm volatile("" : "+s"(ns.p), "+s"(ns.last));
-    }
+    TileSrc ns = src_of(it + AHEAD);             // loaded during this step
+    // materialise the (possibly table-derived) source now: a scalar-load wait
+    // later would also drain the operand reads in flight
+    asm volatile("" : "+s"(ns.p), "+s"(ns.last), "+s"(ns.lastb));
     const int nboff = ((it + AHEAD) % NBUF) * TILE_BYTES;
 
     // ---- softmax of tile it: weights 2^(s - m_ref) (see the reference note
-    // below), two at a time, spread over the score MFMAs of tile it+1 when
-    // there is one. The denominator sums exactly the bf16 weights the value
+    // below), two at a time, spread over the score MFMAs of tile it+1 (the
+    // last step scores the stand-in past the segment's end). The denominator sums exactly the bf16 weights the value
     // MFMAs use (a dot product of each rounded pair with (1, 1)).
     bf16x2 pp[4];  // pair p: positions 4(l/16) + 2(p&1) + {0, 1} of head block p/2
     // Positions past the visible length (last tile only) get weight 0: their
@@ -866,20 +879,15 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
       lsum[hb] = __builtin_amdgcn_fdot2_f32_bf16(q, ones, lsum[hb], false);
     };
     if (owner) {
-      if (it + 1 < ntiles) {
-        scores(((it + 1) % NBUF) * TILE_BYTES, sn, [&](int ks) {
-          if ((ks & 3) == 1) soft2(ks >> 2);
-          if (pre && (ks & 3) == 0) load_tile(ns, nboff, ks >> 2);
-        });
-        sync_scores(sn[0], sn[1]);
-      } else {
-#pragma unroll
-        for (int pi = 0; pi < 4; ++pi) soft2(pi);
-      }
+      // pairs 0..3 after k-steps 1, 5, 9, 13; loads 0..4 after k-steps 0, 4, .., 16
+      scores(((it + 1) % NBUF) * TILE_BYTES, sn, [&](int ks) {
+        if ((ks & 3) == 1 && ks < 16) soft2(ks >> 2);
+        if ((ks & 3) == 0) load_tile(ns, nboff, ks >> 2);
+      });
       const int pw = pwo + (it & 1) * P_BYTES;
       *(MLA_LDS bf16x4*)(smem + pw) = __builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3);
       *(MLA_LDS bf16x4*)(smem + pw + 16 * 32) = __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3);
-    } else if (pre) {
+    } else {
 #pragma unroll
       for (int k = 0; k < 5; ++k) load_tile(ns, nboff, k);
     }
@@ -893,16 +901,8 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
       vb[d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(smem + boff + vB + xo));
     }
 
-    // tile it+2 complete (published by this barrier); later tiles in flight
-    if (it + 2 < ntiles) {
-      const int after = ntiles - it - 3;  // tiles issued after it+2
-      if (after >= AHEAD - 2) {
-        if (wv < 2) wait_vmcnt<(AHEAD - 2) * 5>();
-        else wait_vmcnt<(AHEAD - 2) * 4>();
-      } else {
-        wait_vm(after * L);
-      }
-    }
+    // tile it+2 complete (published by this barrier); tile it+3 in flight
+    wait_tiles<0>(wv);
     wait_lgkm0();
     block_barrier();  // weights of tile it and tile it+2 visible
 
@@ -914,7 +914,7 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) pf[hb] = *(const MLA_LDS bf16x8*)(smem + pr + hb * 32 * 32);
     }
-    if (owner && it + 2 < ntiles) kprefetch(((it + 2) % NBUF) * TILE_BYTES);
+    if (owner) kprefetch(((it + 2) % NBUF) * TILE_BYTES);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
@@ -930,6 +930,7 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
     s0[0] = s1[0];
     s0[1] = s1[1];
   }
+  wait_vmcnt<0>();  // the stand-in tiles' loads end before the ring is reused
 
   // Softmax reference. Each head's reference max m_ref is the largest score
   // of the segment's first tile and the weights are 2^(x - m_ref). Keeping
