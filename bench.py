@@ -170,23 +170,25 @@ def main():
              "latent_decode (attention + combine)": two_call,
              "up_v (W_UV stays in the last-level cache between calls)": upv}
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
     # The attention kernel is timed on every n-th step of the timed region.
     # The dispatch start is taken when the dispatch is picked up, which can be
     # while the kernel before it still drains (a few us of it fall inside the
-    # interval: the measured rate is a lower bound).
+    # interval: the measured rate is a lower bound). The events are created
+    # before the warm-up, so that the GPU does not sit idle between the
+    # warm-up and the timed steps while the host makes them (an idle gap of
+    # tens of ms was followed by slower steps: the chip's clock management).
     every = max(1, args.event_every)
     attn_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(0, args.steps, every)]
-    for a, b_ in attn_ev:  # create the events (lazily created on first record)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    for a, b_ in attn_ev + [(t_start, t_end)]:  # create the events (lazily created on first record)
         a.record(stream)
         b_.record(stream)
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
