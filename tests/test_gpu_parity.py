@@ -90,6 +90,19 @@ def test_decode_split_count_invariance(workers):
     check_decode(case, num_workers=workers, label="split invariance")
 
 
+@pytest.mark.parametrize("H,page_size,workers", [(128, None, 1), (128, None, 5), (128, 16, 9), (64, None, 13),
+                                                  (128, 16, 23)])
+def test_decode_short_segments(H, page_size, workers):
+    """Segments of 1 to 6 tiles, shorter than, equal to and just past the
+    tile pipeline's depth, where the last steps load and score stand-in tiles
+    past the segment's end (rows past each length, and unused page slots,
+    hold NaN, so a read of them would show)."""
+    lens = [16, 32, 48, 64, 80, 96, 15, 47]
+    case = G.decode_case(len(lens), H, 512, 64, lens, G.BF16, seed=90 + workers, page_size=page_size)
+    case.kq_scale = 1.0 / math.sqrt(192)
+    check_decode(case, num_workers=workers, label="short segments")
+
+
 @pytest.mark.parametrize("dtype", [G.BF16, G.F32])
 def test_decode_timing_events(dtype):
     """Timing events passed with the attention launch: the results equal those
