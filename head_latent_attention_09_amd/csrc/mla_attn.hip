@@ -405,11 +405,12 @@ constexpr int SMEM_BYTES = LDS_MFIX + 32 * NW * 4;
 // 32x32x16), so each wave reads a quarter of the tile's values.
 //
 // Software pipeline, one workgroup barrier per tile. Iteration i:
-//   scores of tile i+1, with the softmax of tile i (scores from the previous
-//   iteration) and the loads of tile i+AHEAD placed between the MFMAs;
-//   value fragments of tile i; weights of tile i to LDS; barrier; weight
-//   fragments of tile i and the first score operands of tile i+2; value
-//   product of tile i.
+//   scores of tile i+1, with the loads of tile i+AHEAD between the MFMAs,
+//   and the softmax of tile i (scores from the previous iteration; written
+//   between the MFMAs too, the compiler places most of it after the chain;
+//   forcing it to stay there measured 1-2 % slower); value fragments of tile
+//   i; weights of tile i to LDS; barrier; weight fragments of tile i and the
+//   first score operands of tile i+2; value product of tile i.
 // Tile j is loaded into buffer j % NBUF during iteration j - AHEAD, after the
 // barrier that ends every read of the buffer's previous tile j - NBUF (its
 // value fragments are read, and waited for, before the barrier of iteration
@@ -851,9 +852,10 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
     const int nboff = ((it + AHEAD) % NBUF) * TILE_BYTES;
 
     // ---- softmax of tile it: weights 2^(s - m_ref) (see the reference note
-    // below), two at a time, spread over the score MFMAs of tile it+1 (the
-    // last step scores the stand-in past the segment's end). The denominator sums exactly the bf16 weights the value
-    // MFMAs use (a dot product of each rounded pair with (1, 1)).
+    // below), two at a time, written between the score MFMAs of tile it+1
+    // (the last step scores the stand-in past the segment's end). The
+    // denominator sums exactly the bf16 weights the value MFMAs use (a dot
+    // product of each rounded pair with (1, 1)).
     bf16x2 pp[4];  // pair p: positions 4(l/16) + 2(p&1) + {0, 1} of head block p/2
     // Positions past the visible length (last tile only) get weight 0: their
     // rows repeat the last visible row, so their scores are finite and no
