@@ -33,6 +33,7 @@ namespace mla {
 namespace fa {
 
 constexpr int QB = 128, KB = 64, DN = 128, DV = 128, NT = 256, NW = 4;
+static_assert(NT == 64 * NW && QB == 32 * NW, "four waves of 32 queries each");
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 template <int DR>
