@@ -767,7 +767,7 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
       const int rowb = rb < s.lastb ? rb : s.lastb;
       dma16_tile<STREAM>(s.p, (uint32_t)((dofs ^ (sC(4 * k) << 4)) + rowb), lds_addr(buf + ld * 1024));
     } else if (wv < 2) {
-      const int row = s.last >= TILE - 1 ? rrow : (rrow < s.last ? rrow : s.last);
+      const int row = rrow < s.last ? rrow : s.last;
       dma16_tile<STREAM>(s.p, (uint32_t)(row * (WD * 2) + rdofs), lds_addr(buf + C_BYTES + wv * 1024));
     }
   };
@@ -858,14 +858,15 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
     // product of each rounded pair with (1, 1)).
     bf16x2 pp[4];  // pair p: positions 4(l/16) + 2(p&1) + {0, 1} of head block p/2
     // Positions past the visible length (last tile only) get weight 0: their
-    // rows repeat the last visible row, so their scores are finite and no
-    // larger than a visible one; the bf16 pairs are masked with keep[p & 1].
-    uint32_t keep[2] = {0xffffffffu, 0xffffffffu};
+    // rows repeat the last visible row (finite values for the value product)
+    // and their scores are set to -inf, whose weight 2^-inf is exactly 0.
     if (nvalid < TILE) {
       const int lim = nvalid - 4 * q4;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-        keep[h2] = (2 * h2 < lim ? 0xffffu : 0u) | (2 * h2 + 1 < lim ? 0xffff0000u : 0u);
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          sc[hb][rr] = rr < lim ? sc[hb][rr] : -INFINITY;
     }
     auto soft2 = [&](int p) {
       const int hb = p >> 1, r0 = 2 * (p & 1);
@@ -875,7 +876,6 @@ __device__ __forceinline__ int attend_segment(const Args& a, int r, int len, int
       bf16x2 q;
       q[0] = f32_to_bf16(w0);
       q[1] = f32_to_bf16(w1);
-      q = __builtin_bit_cast(bf16x2, __builtin_bit_cast(uint32_t, q) & keep[p & 1]);
       pp[p] = q;
       const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
       lsum[hb] = __builtin_amdgcn_fdot2_f32_bf16(q, ones, lsum[hb], false);
